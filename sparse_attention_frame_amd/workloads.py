@@ -1,0 +1,87 @@
+"""Seeded synthetic inputs for frame-aligned window-sparse attention.
+
+This module only draws random tensors; it contains none of the attention
+arithmetic. Both the HIP path (through the tests and the bench) and the CPU
+oracle consume exactly the tensors produced here.
+
+The shapes model the self-attention of the super-resolution transformer in
+the Avatar IV pipeline ("HeyGen x Google Cloud: Bringing Avatar IV to TPUs",
+section "Deleting the mask"): one reference frame followed by F latent video
+frames of T tokens each, laid out frame-major, heads independent. Real
+activations are not available, so q and v are standard normal and every key of
+a head carries a shared random offset ``c``, modelling the sizeable component
+that keys have in common according to the section "Unchaining softmax". Values are drawn in fp32
+and rounded to bf16 with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Tuple
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    frames: int            # F: latent video frames (the reference frame is extra)
+    tokens_per_frame: int  # T
+    heads: int             # H
+    head_dim: int          # d
+    window: int            # w: a video frame sees video frames within +-w
+    sigma_c: float         # std-dev of the per-head shared key component
+    seed: int
+    batch: int = 1
+    boost_heads: Tuple[int, ...] = field(default_factory=tuple)  # q and k scaled by boost
+    boost: float = 6.0
+
+    @property
+    def seq(self) -> int:
+        return (self.frames + 1) * self.tokens_per_frame
+
+    def with_window(self, w: int, name: str | None = None) -> "Workload":
+        return replace(self, window=w, name=name or f"{self.name}_w{w}")
+
+
+TINY = Workload("tiny", frames=4, tokens_per_frame=48, heads=2, head_dim=64,
+                window=1, sigma_c=2.0, seed=1000)
+SMALL = Workload("small", frames=8, tokens_per_frame=208, heads=8, head_dim=128,
+                 window=2, sigma_c=3.0, seed=1001)
+P720 = Workload("720p", frames=13, tokens_per_frame=3600, heads=12, head_dim=128,
+                window=2, sigma_c=3.0, seed=1002)
+P1080 = Workload("1080p", frames=5, tokens_per_frame=8160, heads=12, head_dim=128,
+                 window=1, sigma_c=3.0, seed=1003)
+STRESS = Workload("stress", frames=13, tokens_per_frame=3600, heads=16, head_dim=128,
+                  window=2, sigma_c=3.0, seed=1004, boost_heads=(3, 7, 11, 15))
+STRESS_FULL = STRESS.with_window(13, "stress_w13")
+
+ALL = {w.name: w for w in (TINY, SMALL, P720, P1080, STRESS, STRESS_FULL)}
+
+
+def make_inputs_np(wl: Workload):
+    """q, k, v as float32 numpy arrays [B, S, H, d] holding bf16-representable values."""
+    import torch
+
+    rng = np.random.default_rng(wl.seed)
+    shape = (wl.batch, wl.seq, wl.heads, wl.head_dim)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    c = rng.standard_normal((wl.batch, wl.heads, wl.head_dim), dtype=np.float32)
+    c *= np.float32(wl.sigma_c)
+    k += c[:, None, :, :]
+    for h in wl.boost_heads:
+        q[:, :, h, :] *= np.float32(wl.boost)
+        k[:, :, h, :] *= np.float32(wl.boost)
+    out = []
+    for x in (q, k, v):
+        # torch's float32 -> bfloat16 cast rounds to nearest even
+        out.append(torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy())
+    return tuple(out)
+
+
+def make_inputs(wl: Workload):
+    """q, k, v as contiguous torch.bfloat16 CPU tensors [B, S, H, d]."""
+    import torch
+
+    return tuple(torch.from_numpy(x).to(torch.bfloat16) for x in make_inputs_np(wl))
