@@ -1,0 +1,163 @@
+"""Benchmark: one step = the whole hot path (norm array + attention kernel) over the
+720p-shaped layer (reference frame + 13 frames x 3600 tokens, 12 heads, d = 128,
+window +-2, batch 1) on one MI355X. Prints one JSON line.
+
+value  = active-block TFLOP/s of the step: 4*d flops per visible (query, key)
+         pair, divided by the wall time per step (sfa_norms + sfa_fwd).
+roofline = the attention kernel alone, timed with HIP events on its stream,
+         against the bf16 dense MFMA peak.
+cpu_baseline = the fp64 CPU oracle on a bounded sample of the same layer.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "active-block attention TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (no sparsity)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_720p.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, q_np, k_np, v_np, budget_s=12.0):
+    """Time the oracle (as it stands) on whole query frames of head 0 until ~budget_s."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    T, F, d = wl.tokens_per_frame, wl.frames, wl.head_dim
+    order = [F // 2] + [f for f in range(F + 1) if f != F // 2]   # a full-window frame first
+    flops = 0.0
+    done = []
+    t0 = time.perf_counter()
+    for f in order:
+        rows = np.arange(f * T, (f + 1) * T)
+        oracle.attention_rows(q_np, k_np, v_np, F, T, wl.window, 0, 0, rows)
+        nkeys = len(oracle.key_frames(f, F, wl.window)) * T
+        flops += 4.0 * d * T * nkeys
+        done.append(f)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"head 0, query frames {done} ({len(done) * T} rows) of the 720p layer, "
+                      f"fp64 dense-masked numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="720p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_frame_amd as sfa
+    from sparse_attention_frame_amd import workloads as W
+
+    wl = W.ALL[args.workload]
+    log(f"bench: generating {wl.name} inputs")
+    q_np, k_np, v_np = W.make_inputs_np(wl)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q_np, k_np, v_np))
+    plan = sfa.Plan.for_workload(wl)
+    ws = plan.workspace(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sfa.norms(plan, q, k, workspace=ws, stream=stream)
+        sfa.fwd(plan, q, k, v, out=out, workspace=ws, stream=stream)
+
+    log("bench: warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        sfa.norms(plan, q, k, workspace=ws, stream=stream)
+        e[1].record(stream)
+        sfa.fwd(plan, q, k, v, out=out, workspace=ws, stream=stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    norms_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    fwd_min = float(np.min([e[1].elapsed_time(e[2]) for e in ev]))
+
+    info = plan.info
+    flops = info["active_flops"]
+    value = flops / (ms_step * 1e-3) / 1e12
+    fwd_tf = flops / (fwd_ms * 1e-3) / 1e12
+    st = sfa.head_stats(plan, ws)
+    assert torch.isfinite(out.float()).all(), "non-finite output"
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}-shaped layer: reference frame + F={wl.frames} frames x "
+                               f"T={wl.tokens_per_frame} tokens (S={wl.seq}), H={wl.heads}, "
+                               f"d={wl.head_dim}, window +-{wl.window}, batch {wl.batch}",
+                   "block_q": info["block_q"], "items": info["items"],
+                   "active_gflop": round(flops / 1e9, 1),
+                   "eligible_heads": int(st["eligible"].sum()), "heads": wl.heads},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_min_ms": round(fwd_min, 4),
+        "norms_ms": round(norms_ms, 4),
+        "roofline": {"bound": "mfma", "kernel": "fwd_kernel<128>",
+                     "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(wl, q_np, k_np, v_np)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

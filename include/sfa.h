@@ -1,0 +1,146 @@
+/*
+ * sfa.h -- C ABI of the frame-aligned window-sparse attention library (gfx950).
+ *
+ * The operation ("HeyGen x Google Cloud: Bringing Avatar IV to TPUs"):
+ *   - tokens are frame-major: frame 0 is the global reference frame, frames
+ *     1..F are video frames, each of T tokens; S = (F + 1) * T;
+ *   - a query of video frame v sees the keys of the reference frame and of
+ *     the video frames max(1, v - w) .. min(F, v + w); a reference-frame query
+ *     sees the reference frame only (section "Deleting the mask", Fig. 3);
+ *   - O_i = sum_j softmax_j(scale * <q_i, k_j>) v_j over the visible keys;
+ *   - heads whose Cauchy-Schwarz bound  scale * max_i ||q_i|| * max_j ||k_j - mu||
+ *     (mu = per-head key mean) is <= bound_limit use that bound as a fixed
+ *     softmax maximum; the others use the online (running-maximum) softmax in
+ *     the same kernel (section "Unchaining softmax", Fig. 4);
+ *   - QK^T and PV run on bf16 MFMA with fp32 accumulation; P is rounded to
+ *     bf16 before PV (section "Proving pixels unchanged").
+ *
+ * Conventions for every entry point:
+ *   - returns an int status (SFA_OK = 0 or a negative SFA_ERR_*), never throws,
+ *     never aborts; on error nothing has been enqueued;
+ *   - device pointers (tensor data, workspace) are owned by the caller; the
+ *     library never allocates or frees device memory;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); work
+ *     is enqueued asynchronously on it; only sfa_read_head_stats synchronises;
+ *   - a plan owns host memory only, is immutable after creation and may be
+ *     shared by threads.
+ */
+#ifndef SFA_H
+#define SFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SFA_OK 0
+#define SFA_ERR_INVALID (-1)     /* null pointer, bad size, too-small workspace */
+#define SFA_ERR_UNSUPPORTED (-2) /* T % 16 != 0, head_dim not 64/128, misaligned data */
+#define SFA_ERR_HIP (-3)         /* HIP launch/runtime error (see sfa_status_str) */
+#define SFA_ERR_NOMEM (-4)       /* host allocation failed */
+
+/* Attention geometry. One plan per geometry (section "Workload and porting":
+ * every attention is dispatched to a kernel shaped for it). */
+typedef struct sfa_geometry {
+  int32_t batch;            /* B >= 1 */
+  int32_t heads;            /* H >= 1 */
+  int32_t head_dim;         /* d: 64 or 128 */
+  int32_t frames;           /* F >= 0 video frames; the reference frame is extra */
+  int32_t tokens_per_frame; /* T >= 16, T % 16 == 0 */
+  int32_t window;           /* w >= 0 */
+  float scale;              /* softmax scale; 0 selects 1/sqrt(d) */
+  float bound_limit;        /* fixed-max eligibility threshold (40 in the workloads);
+                               a negative value makes every head use the online path */
+} sfa_geometry;
+
+/* A bf16 tensor [B, S, H, d] addressed as
+ * data + b*stride_b + s*stride_s + h*stride_h + e  (strides in elements, d contiguous).
+ * data must be 16-byte aligned and every stride a multiple of 8. */
+typedef struct sfa_tensor {
+  void* data;
+  int64_t stride_b;
+  int64_t stride_s;
+  int64_t stride_h;
+} sfa_tensor;
+
+typedef struct sfa_plan sfa_plan;
+
+typedef struct sfa_plan_info {
+  int32_t block_q;          /* query rows per work item; divides T, multiple of 16 */
+  int32_t granule;          /* token granule of the key loop (16) */
+  int32_t waves_per_item;   /* 64-lane waves in one workgroup */
+  int32_t items;            /* work items = B * H * (F + 1) * (T / block_q) */
+  int64_t active_pairs;     /* visible (query, key) pairs summed over B and H */
+  double active_flops;      /* 4 * d * active_pairs (q.k and p.v, 2 flops per MAC) */
+  int64_t io_bytes;         /* q, k, v read once and o written once: 8 * B * S * H * d */
+  size_t workspace_bytes;   /* device workspace needed by sfa_norms / sfa_fwd */
+} sfa_plan_info;
+
+/* Validates the geometry and builds the work decomposition (host only, no HIP
+ * call, no device memory). *out is set to NULL on error. */
+int sfa_plan_create(const sfa_geometry* geom, sfa_plan** out);
+
+/* Same, forcing the query rows per work item (0 = automatic). block_q must be a
+ * multiple of 16 that divides T and is at most 256 (else SFA_ERR_UNSUPPORTED). */
+int sfa_plan_create_tiled(const sfa_geometry* geom, int32_t block_q, sfa_plan** out);
+
+void sfa_plan_destroy(sfa_plan* plan);
+
+int sfa_plan_get_info(const sfa_plan* plan, sfa_plan_info* out);
+
+/* Key token ranges seen by queries of `query_frame` (0 = reference frame), as
+ * half-open [start, end) pairs in ranges[0..2*n). Adjacent ranges are merged,
+ * so n is 1 or 2. Section "Deleting the mask": every range is a whole number of
+ * frames, hence a whole number of 16-token granules. */
+int sfa_plan_key_ranges(const sfa_plan* plan, int32_t query_frame, int32_t ranges[4],
+                        int32_t* n);
+
+/* Work item scheduled at position `index` of the launch (0 <= index < items):
+ * writes {batch, head, query_frame, query_block}. Items are ordered by
+ * decreasing key count (largest first) and grouped so that the items sharing
+ * one (batch, head, frame) key stream land on one XCD. */
+int sfa_plan_item(const sfa_plan* plan, int32_t index, int32_t item[4]);
+
+/* Precompute the norm array for the fixed maximum (section "Unchaining
+ * softmax"): per (b, h) the key mean mu, max_j ||k_j - mu||, max_i ||q_i||,
+ * the bound and the eligibility flag; per row ||q_i|| and <q_i, mu>. Reads q
+ * and k once and k a second time; fp32; writes only into `workspace`.
+ * Deterministic (fixed reduction order, no atomics). */
+int sfa_norms(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* The attention kernel: one pass over each query block's reference-frame and
+ * window key granules, fixed maximum for eligible heads, online softmax for the
+ * others. Requires sfa_norms to have run on the same q, k and workspace earlier
+ * on the stream. o may not alias q, k or v. */
+int sfa_fwd(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_tensor o,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* sfa_norms followed by sfa_fwd. */
+int sfa_attention(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v,
+                  sfa_tensor o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Copies per-head statistics out of the workspace after sfa_norms (synchronises
+ * the stream). Each output pointer is host memory of B*H entries (mu: B*H*d) or
+ * NULL to skip it. */
+int sfa_read_head_stats(const sfa_plan* plan, const void* workspace, float* mu, float* kmax,
+                        float* qmax, float* bound, uint8_t* eligible, void* stream);
+
+/* Copies the per-row half of the norm array after sfa_norms (synchronises the
+ * stream): qnorm[b][h][s] = ||q_s|| and qmu[b][h][s] = <q_s, mu_bh>, B*H*S floats
+ * each, host memory, either may be NULL. The attention kernel derives the fixed
+ * row maximum from them as M = scale * (qmu + qnorm * kmax). */
+int sfa_read_row_norms(const sfa_plan* plan, const void* workspace, float* qnorm, float* qmu,
+                       void* stream);
+
+/* Human-readable text for a status code (includes the last HIP error of the
+ * calling thread for SFA_ERR_HIP). */
+const char* sfa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFA_H */

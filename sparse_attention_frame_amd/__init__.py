@@ -1,0 +1,21 @@
+"""Frame-aligned window-sparse attention on MI355X (gfx950).
+
+The computation lives in libsfa.so (hand-written HIP kernels behind the C ABI
+of include/sfa.h); this package only loads it and marshals torch tensors.
+Importing the package does not need a GPU; calling the kernels does, and
+raises if the library was not built.
+"""
+from ._lib import SfaError, lib  # noqa: F401
+from .api import (  # noqa: F401
+    Plan,
+    attention,
+    fwd,
+    head_stats,
+    norms,
+    row_norms,
+    sfa_attention,
+    sfa_fwd,
+    sfa_norms,
+    sfa_read_head_stats,
+    sfa_read_row_norms,
+)

@@ -1,0 +1,175 @@
+"""Python face of the C ABI in include/sfa.h (same names; marshalling only).
+
+Tensors are torch.bfloat16 device tensors shaped [B, S, H, d] with the last
+dimension contiguous; any batch/token/head strides (multiples of 8 elements)
+are passed through, so BHSD storage or a head-subset view works unchanged.
+torch supplies device memory and the stream; every step of the computation
+runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import Geometry, PlanInfo, Tensor, check, lib
+
+
+def _stream_ptr(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """sfa_plan_create: geometry -> tiles and the largest-first work-item order."""
+
+    def __init__(self, batch: int, heads: int, head_dim: int, frames: int,
+                 tokens_per_frame: int, window: int, scale: float = 0.0,
+                 bound_limit: float = 40.0, block_q: int = 0):
+        self.geometry = Geometry(batch, heads, head_dim, frames, tokens_per_frame, window,
+                                 scale, bound_limit)
+        handle = ctypes.c_void_p()
+        L = lib()
+        if block_q:
+            st = L.sfa_plan_create_tiled(ctypes.byref(self.geometry), block_q,
+                                         ctypes.byref(handle))
+        else:
+            st = L.sfa_plan_create(ctypes.byref(self.geometry), ctypes.byref(handle))
+        check(st, "sfa_plan_create")
+        self._h = handle
+        info = PlanInfo()
+        check(L.sfa_plan_get_info(self._h, ctypes.byref(info)), "sfa_plan_get_info")
+        self.info = {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+        self.seq = (frames + 1) * tokens_per_frame
+
+    @classmethod
+    def for_workload(cls, wl, **kw):
+        return cls(wl.batch, wl.heads, wl.head_dim, wl.frames, wl.tokens_per_frame, wl.window,
+                   **kw)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib._lib is not None:
+            _lib._lib.sfa_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def key_ranges(self, frame: int):
+        r = (ctypes.c_int32 * 4)()
+        n = ctypes.c_int32()
+        check(lib().sfa_plan_key_ranges(self._h, frame, r, ctypes.byref(n)),
+              "sfa_plan_key_ranges")
+        return [(r[2 * i], r[2 * i + 1]) for i in range(n.value)]
+
+    def item(self, index: int):
+        out = (ctypes.c_int32 * 4)()
+        check(lib().sfa_plan_item(self._h, index, out), "sfa_plan_item")
+        return tuple(out)
+
+    def workspace(self, device=None):
+        import torch
+
+        return torch.empty(self.info["workspace_bytes"], dtype=torch.uint8,
+                           device=device or "cuda")
+
+
+def as_tensor(t, plan: Plan, name: str) -> Tensor:
+    import torch
+
+    g = plan.geometry
+    shape = (g.batch, plan.seq, g.heads, g.head_dim)
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be torch.bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, plan expects {shape}")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} needs a contiguous head dimension")
+    return Tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ws(plan, workspace, device):
+    if workspace is None:
+        workspace = plan.workspace(device)
+    return workspace
+
+
+def sfa_norms(plan: Plan, q, k, workspace=None, stream=None):
+    ws = _ws(plan, workspace, q.device)
+    check(lib().sfa_norms(plan.handle, as_tensor(q, plan, "q"), as_tensor(k, plan, "k"),
+                          ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)),
+          "sfa_norms")
+    return ws
+
+
+def sfa_fwd(plan: Plan, q, k, v, out=None, workspace=None, stream=None):
+    import torch
+
+    if workspace is None:
+        raise ValueError("sfa_fwd needs the workspace filled by sfa_norms")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    check(lib().sfa_fwd(plan.handle, as_tensor(q, plan, "q"), as_tensor(k, plan, "k"),
+                        as_tensor(v, plan, "v"), as_tensor(out, plan, "o"),
+                        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                        _stream_ptr(stream)), "sfa_fwd")
+    return out
+
+
+def sfa_attention(plan: Plan, q, k, v, out=None, workspace=None, stream=None):
+    """sfa_norms + sfa_fwd on one stream. Returns (out, workspace)."""
+    import torch
+
+    ws = _ws(plan, workspace, q.device)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    check(lib().sfa_attention(plan.handle, as_tensor(q, plan, "q"), as_tensor(k, plan, "k"),
+                              as_tensor(v, plan, "v"), as_tensor(out, plan, "o"),
+                              ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)),
+          "sfa_attention")
+    return out, ws
+
+
+def sfa_read_head_stats(plan: Plan, workspace, stream=None):
+    g = plan.geometry
+    bh = g.batch * g.heads
+    mu = np.empty((g.batch, g.heads, g.head_dim), np.float32)
+    kmax = np.empty((g.batch, g.heads), np.float32)
+    qmax = np.empty((g.batch, g.heads), np.float32)
+    bound = np.empty((g.batch, g.heads), np.float32)
+    elig = np.empty((g.batch, g.heads), np.uint8)
+    f = ctypes.POINTER(ctypes.c_float)
+    check(lib().sfa_read_head_stats(plan.handle, ctypes.c_void_p(workspace.data_ptr()),
+                                    mu.ctypes.data_as(f), kmax.ctypes.data_as(f),
+                                    qmax.ctypes.data_as(f), bound.ctypes.data_as(f),
+                                    elig.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                    _stream_ptr(stream)), "sfa_read_head_stats")
+    assert bh == kmax.size
+    return {"mu": mu, "kmax": kmax, "qmax": qmax, "bound": bound, "eligible": elig.astype(bool)}
+
+
+def sfa_read_row_norms(plan: Plan, workspace, stream=None):
+    g = plan.geometry
+    qn = np.empty((g.batch, g.heads, plan.seq), np.float32)
+    qmu = np.empty((g.batch, g.heads, plan.seq), np.float32)
+    f = ctypes.POINTER(ctypes.c_float)
+    check(lib().sfa_read_row_norms(plan.handle, ctypes.c_void_p(workspace.data_ptr()),
+                                   qn.ctypes.data_as(f), qmu.ctypes.data_as(f),
+                                   _stream_ptr(stream)), "sfa_read_row_norms")
+    return qn, qmu
+
+
+# short aliases
+norms = sfa_norms
+fwd = sfa_fwd
+attention = sfa_attention
+head_stats = sfa_read_head_stats
+row_norms = sfa_read_row_norms

@@ -1,0 +1,319 @@
+// C ABI: planning (host only), argument validation and kernel launches.
+//
+// Planning follows "HeyGen x Google Cloud: Bringing Avatar IV to TPUs",
+// section "Deleting the mask": query blocks are whole 16-token granules that
+// divide the frame span T, so every (query block, key granule) pair is either
+// fully visible or skipped and the key loop never needs a mask or padding.
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "sfa_internal.h"
+
+using namespace sfa;
+
+namespace {
+
+thread_local hipError_t g_last_hip = hipSuccess;
+thread_local char g_msg[256];
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return SFA_OK;
+  g_last_hip = e;
+  return SFA_ERR_HIP;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int validate_geometry(const sfa_geometry* g) {
+  if (!g) return SFA_ERR_INVALID;
+  if (g->batch < 1 || g->heads < 1 || g->frames < 0 || g->window < 0 ||
+      g->tokens_per_frame < 1)
+    return SFA_ERR_INVALID;
+  if (!(g->scale >= 0.0f) || !isfinite(g->scale) || isnan(g->bound_limit))
+    return SFA_ERR_INVALID;
+  if (g->head_dim != 64 && g->head_dim != 128) return SFA_ERR_UNSUPPORTED;
+  if (g->tokens_per_frame % kGranule != 0) return SFA_ERR_UNSUPPORTED;
+  if (g->frames + 1 > kMaxFrameSlots) return SFA_ERR_UNSUPPORTED;
+  const int64_t S = int64_t(g->frames + 1) * g->tokens_per_frame;
+  // 32-bit token and row indices inside the kernels
+  if (S * g->heads * int64_t(g->batch) > (int64_t(1) << 31) - 1) return SFA_ERR_UNSUPPORTED;
+  return SFA_OK;
+}
+
+// Query granules per work item: the largest divisor of T/16 that fits one
+// workgroup (4 waves x 4 sub-tiles of 16 rows).
+int auto_block_granules(int t_granules) {
+  for (int g = kMaxBlockGranules; g >= 1; --g)
+    if (t_granules % g == 0) return g;
+  return 1;
+}
+
+int create(const sfa_geometry* geom, int32_t block_q, sfa_plan** out) {
+  if (!out) return SFA_ERR_INVALID;
+  *out = nullptr;
+  int st = validate_geometry(geom);
+  if (st != SFA_OK) return st;
+  const int T = geom->tokens_per_frame;
+  const int tg = T / kGranule;
+  int gq;
+  if (block_q == 0) {
+    gq = auto_block_granules(tg);
+  } else {
+    if (block_q < 0 || block_q % kGranule != 0 || T % block_q != 0 ||
+        block_q / kGranule > kMaxBlockGranules)
+      return SFA_ERR_UNSUPPORTED;
+    gq = block_q / kGranule;
+  }
+  sfa_plan* p = new (std::nothrow) sfa_plan;
+  if (!p) return SFA_ERR_NOMEM;
+  memset(p, 0, sizeof(*p));
+  p->g = *geom;
+  const int F = geom->frames, w = geom->window, B = geom->batch, H = geom->heads;
+  const int D = geom->head_dim;
+  p->scale = geom->scale == 0.0f ? 1.0f / sqrtf(float(D)) : geom->scale;
+  p->S = (F + 1) * T;
+  p->gq = gq;
+  p->nqb = tg / gq;
+  p->items = B * H * (F + 1) * p->nqb;
+  p->nchunk = (p->S + kNormChunk - 1) / kNormChunk;
+
+  // frames by decreasing cost (number of visible frames), ties by frame index
+  for (int f = 0; f <= F; ++f) p->frame_order[f] = uint16_t(f);
+  std::stable_sort(p->frame_order, p->frame_order + F + 1, [&](uint16_t a, uint16_t b) {
+    return visible_frames(a, F, w) > visible_frames(b, F, w);
+  });
+  int64_t frame_pairs = 0;
+  for (int f = 0; f <= F; ++f) frame_pairs += visible_frames(f, F, w);
+  p->active_pairs = frame_pairs * int64_t(T) * T * B * H;
+
+  // workspace layout (all fp32 unless noted), 256-byte aligned sections
+  const size_t bh = size_t(B) * H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  p->ws.mu = take(bh * D * 4);
+  p->ws.kmax = take(bh * 4);
+  p->ws.qmax = take(bh * 4);
+  p->ws.bound = take(bh * 4);
+  p->ws.elig = take(bh);                       // uint8
+  p->ws.qn = take(bh * size_t(p->S) * 4);      // [b][h][s]
+  p->ws.qmu = take(bh * size_t(p->S) * 4);     // [b][h][s]
+  p->ws.psum = take(size_t(p->nchunk) * bh * D * 4);  // [chunk][b][h][d]
+  p->ws.pkmax = take(size_t(p->nchunk) * bh * 4);     // [chunk][b][h], squared norms
+  p->ws.pqmax = take(size_t(p->nchunk) * bh * 4);
+  p->ws.total = off;
+  *out = p;
+  return SFA_OK;
+}
+
+int check_tensor(const sfa_tensor& t) {
+  if (!t.data) return SFA_ERR_INVALID;
+  if (t.stride_b < 0 || t.stride_s < 0 || t.stride_h < 0) return SFA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(t.data) & 15) != 0) return SFA_ERR_UNSUPPORTED;
+  if ((t.stride_b | t.stride_s | t.stride_h) & 7) return SFA_ERR_UNSUPPORTED;
+  return SFA_OK;
+}
+
+bool ranges_overlap(const sfa_plan* p, const sfa_tensor& a, const sfa_tensor& b) {
+  // conservative byte extents of two strided tensors
+  auto extent = [&](const sfa_tensor& t, uintptr_t* lo, uintptr_t* hi) {
+    const int64_t last = int64_t(p->g.batch - 1) * t.stride_b + int64_t(p->S - 1) * t.stride_s +
+                         int64_t(p->g.heads - 1) * t.stride_h + p->g.head_dim;
+    *lo = reinterpret_cast<uintptr_t>(t.data);
+    *hi = *lo + uintptr_t(last) * 2;
+  };
+  uintptr_t alo, ahi, blo, bhi;
+  extent(a, &alo, &ahi);
+  extent(b, &blo, &bhi);
+  return alo < bhi && blo < ahi;
+}
+
+NormParams norm_params(const sfa_plan* p, const sfa_tensor& q, const sfa_tensor& k, void* ws) {
+  char* base = static_cast<char*>(ws);
+  NormParams n;
+  n.q = static_cast<const uint16_t*>(q.data);
+  n.k = static_cast<const uint16_t*>(k.data);
+  n.qsb = q.stride_b; n.qss = q.stride_s; n.qsh = q.stride_h;
+  n.ksb = k.stride_b; n.kss = k.stride_s; n.ksh = k.stride_h;
+  n.mu = reinterpret_cast<float*>(base + p->ws.mu);
+  n.kmax = reinterpret_cast<float*>(base + p->ws.kmax);
+  n.qmax = reinterpret_cast<float*>(base + p->ws.qmax);
+  n.bound = reinterpret_cast<float*>(base + p->ws.bound);
+  n.elig = reinterpret_cast<uint8_t*>(base + p->ws.elig);
+  n.qn = reinterpret_cast<float*>(base + p->ws.qn);
+  n.qmu = reinterpret_cast<float*>(base + p->ws.qmu);
+  n.psum = reinterpret_cast<float*>(base + p->ws.psum);
+  n.pkmax = reinterpret_cast<float*>(base + p->ws.pkmax);
+  n.pqmax = reinterpret_cast<float*>(base + p->ws.pqmax);
+  n.B = p->g.batch; n.H = p->g.heads; n.S = p->S; n.D = p->g.head_dim;
+  n.nchunk = p->nchunk;
+  n.scale = p->scale;
+  n.bound_limit = p->g.bound_limit;
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sfa_plan_create(const sfa_geometry* geom, sfa_plan** out) { return create(geom, 0, out); }
+
+int sfa_plan_create_tiled(const sfa_geometry* geom, int32_t block_q, sfa_plan** out) {
+  return create(geom, block_q, out);
+}
+
+void sfa_plan_destroy(sfa_plan* plan) { delete plan; }
+
+int sfa_plan_get_info(const sfa_plan* p, sfa_plan_info* out) {
+  if (!p || !out) return SFA_ERR_INVALID;
+  out->block_q = p->gq * kGranule;
+  out->granule = kGranule;
+  out->waves_per_item = kFwdWaves;
+  out->items = p->items;
+  out->active_pairs = p->active_pairs;
+  out->active_flops = 4.0 * p->g.head_dim * double(p->active_pairs);
+  out->io_bytes = int64_t(8) * p->g.batch * p->S * p->g.heads * p->g.head_dim;
+  out->workspace_bytes = p->ws.total;
+  return SFA_OK;
+}
+
+int sfa_plan_key_ranges(const sfa_plan* p, int32_t f, int32_t ranges[4], int32_t* n) {
+  if (!p || !ranges || !n) return SFA_ERR_INVALID;
+  if (f < 0 || f > p->g.frames) return SFA_ERR_INVALID;
+  const KeyRanges r = key_ranges(f, p->g.frames, p->g.tokens_per_frame, p->g.window);
+  ranges[0] = 0;
+  ranges[1] = r.r0_end;
+  if (r.r1_end > r.r1_begin) {
+    ranges[2] = r.r1_begin;
+    ranges[3] = r.r1_end;
+    *n = 2;
+  } else {
+    ranges[2] = ranges[3] = 0;
+    *n = 1;
+  }
+  return SFA_OK;
+}
+
+int sfa_plan_item(const sfa_plan* p, int32_t index, int32_t item[4]) {
+  if (!p || !item || index < 0 || index >= p->items) return SFA_ERR_INVALID;
+  const Item it = decode_item(index, p->frame_order, p->g.batch, p->g.heads, p->nqb, p->items);
+  item[0] = it.b;
+  item[1] = it.h;
+  item[2] = it.f;
+  item[3] = it.qb;
+  return SFA_OK;
+}
+
+int sfa_norms(const sfa_plan* p, sfa_tensor q, sfa_tensor k, void* ws, size_t ws_bytes,
+              void* stream) {
+  if (!p || !ws) return SFA_ERR_INVALID;
+  if (ws_bytes < p->ws.total) return SFA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return SFA_ERR_UNSUPPORTED;
+  int st = check_tensor(q);
+  if (st == SFA_OK) st = check_tensor(k);
+  if (st != SFA_OK) return st;
+  const NormParams n = norm_params(p, q, k, ws);
+  return hip_status(sfa_launch_norms(n, static_cast<hipStream_t>(stream)));
+}
+
+int sfa_fwd(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_tensor o, void* ws,
+            size_t ws_bytes, void* stream) {
+  if (!p || !ws) return SFA_ERR_INVALID;
+  if (ws_bytes < p->ws.total) return SFA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return SFA_ERR_UNSUPPORTED;
+  int st = check_tensor(q);
+  if (st == SFA_OK) st = check_tensor(k);
+  if (st == SFA_OK) st = check_tensor(v);
+  if (st == SFA_OK) st = check_tensor(o);
+  if (st != SFA_OK) return st;
+  if (ranges_overlap(p, o, q) || ranges_overlap(p, o, k) || ranges_overlap(p, o, v))
+    return SFA_ERR_INVALID;
+  char* base = static_cast<char*>(ws);
+  FwdParams f;
+  f.q = static_cast<const uint16_t*>(q.data);
+  f.k = static_cast<const uint16_t*>(k.data);
+  f.v = static_cast<const uint16_t*>(v.data);
+  f.o = static_cast<uint16_t*>(o.data);
+  f.qsb = q.stride_b; f.qss = q.stride_s; f.qsh = q.stride_h;
+  f.ksb = k.stride_b; f.kss = k.stride_s; f.ksh = k.stride_h;
+  f.vsb = v.stride_b; f.vss = v.stride_s; f.vsh = v.stride_h;
+  f.osb = o.stride_b; f.oss = o.stride_s; f.osh = o.stride_h;
+  f.qn = reinterpret_cast<const float*>(base + p->ws.qn);
+  f.qmu = reinterpret_cast<const float*>(base + p->ws.qmu);
+  f.kmax = reinterpret_cast<const float*>(base + p->ws.kmax);
+  f.elig = reinterpret_cast<const uint8_t*>(base + p->ws.elig);
+  f.B = p->g.batch; f.H = p->g.heads; f.S = p->S; f.T = p->g.tokens_per_frame;
+  f.F = p->g.frames; f.w = p->g.window;
+  f.gq = p->gq; f.nqb = p->nqb; f.items = p->items;
+  f.c = p->scale * 1.4426950408889634f;
+  memcpy(f.frame_order, p->frame_order, sizeof(f.frame_order));
+  return hip_status(sfa_launch_fwd(f, p->g.head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int sfa_attention(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_tensor o,
+                  void* ws, size_t ws_bytes, void* stream) {
+  int st = sfa_norms(p, q, k, ws, ws_bytes, stream);
+  if (st != SFA_OK) return st;
+  return sfa_fwd(p, q, k, v, o, ws, ws_bytes, stream);
+}
+
+int sfa_read_head_stats(const sfa_plan* p, const void* ws, float* mu, float* kmax, float* qmax,
+                        float* bound, uint8_t* eligible, void* stream) {
+  if (!p || !ws) return SFA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* base = static_cast<const char*>(ws);
+  const size_t bh = size_t(p->g.batch) * p->g.heads;
+  struct {
+    void* dst;
+    size_t off, bytes;
+  } copies[5] = {{mu, p->ws.mu, bh * p->g.head_dim * 4},
+                 {kmax, p->ws.kmax, bh * 4},
+                 {qmax, p->ws.qmax, bh * 4},
+                 {bound, p->ws.bound, bh * 4},
+                 {eligible, p->ws.elig, bh}};
+  for (auto& c : copies) {
+    if (!c.dst) continue;
+    hipError_t e = hipMemcpyAsync(c.dst, base + c.off, c.bytes, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(hipStreamSynchronize(s));
+}
+
+int sfa_read_row_norms(const sfa_plan* p, const void* ws, float* qnorm, float* qmu,
+                       void* stream) {
+  if (!p || !ws) return SFA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* base = static_cast<const char*>(ws);
+  const size_t bytes = size_t(p->g.batch) * p->g.heads * size_t(p->S) * 4;
+  hipError_t e = hipSuccess;
+  if (qnorm) e = hipMemcpyAsync(qnorm, base + p->ws.qn, bytes, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && qmu)
+    e = hipMemcpyAsync(qmu, base + p->ws.qmu, bytes, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return hip_status(e);
+}
+
+const char* sfa_status_str(int status) {
+  switch (status) {
+    case SFA_OK: return "ok";
+    case SFA_ERR_INVALID: return "invalid argument (null pointer, bad size or workspace too small)";
+    case SFA_ERR_UNSUPPORTED:
+      return "unsupported (T % 16 != 0, head_dim not 64/128, misaligned pointer or stride)";
+    case SFA_ERR_NOMEM: return "host allocation failed";
+    case SFA_ERR_HIP:
+      snprintf(g_msg, sizeof(g_msg), "HIP error %d: %s", int(g_last_hip),
+               hipGetErrorString(g_last_hip));
+      return g_msg;
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

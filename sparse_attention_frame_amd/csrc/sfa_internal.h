@@ -1,0 +1,147 @@
+// Internal definitions shared by the host planner and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sfa.h"
+
+namespace sfa {
+
+constexpr int kGranule = 16;       // token granule: finest bf16 row tiling of the MFMA
+constexpr int kMaxFrameSlots = 1024;  // F + 1 limit (frame order table travels in kernel args)
+constexpr int kFwdWaves = 4;       // waves per attention workgroup
+constexpr int kFwdSub = 4;         // 16-row query sub-tiles per wave
+constexpr int kMaxBlockGranules = kFwdWaves * kFwdSub;  // <= 256 query rows per item
+constexpr int kNormChunk = 64;     // tokens per block in the norm kernels
+
+// Visible key ranges of one query frame: [0, r0_end) and [r1_begin, r1_end)
+// (r1 empty when the window touches frame 1 and the ranges merge).
+struct KeyRanges {
+  int32_t r0_end;
+  int32_t r1_begin;
+  int32_t r1_end;
+};
+
+__host__ __device__ inline KeyRanges key_ranges(int f, int F, int T, int w) {
+  KeyRanges r;
+  if (f == 0) {
+    r.r0_end = T;
+    r.r1_begin = T;
+    r.r1_end = T;
+    return r;
+  }
+  const int lo = f - w > 1 ? f - w : 1;
+  const int hi = f + w < F ? f + w : F;
+  if (lo == 1) {
+    r.r0_end = (hi + 1) * T;
+    r.r1_begin = r.r0_end;
+    r.r1_end = r.r0_end;
+  } else {
+    r.r0_end = T;
+    r.r1_begin = lo * T;
+    r.r1_end = (hi + 1) * T;
+  }
+  return r;
+}
+
+// Number of frames whose keys frame f sees (the cost of its work items).
+__host__ __device__ inline int visible_frames(int f, int F, int w) {
+  if (f == 0) return 1;
+  const int lo = f - w > 1 ? f - w : 1;
+  const int hi = f + w < F ? f + w : F;
+  return 1 + (hi - lo + 1);
+}
+
+struct Item {
+  int32_t b, h, f, qb;
+};
+
+// blockIdx -> work item. Groups of `nqb` items share one (frame, batch, head)
+// key stream; groups are sorted by decreasing cost (frame_order). Workgroups
+// are handed to the 8 XCDs round-robin, so inside every run of 8 groups the
+// index is permuted to give each XCD one whole group (shared K/V in its L2)
+// while the launch order still follows decreasing cost.
+__host__ __device__ inline Item decode_item(int idx, const uint16_t* frame_order, int B, int H,
+                                            int nqb, int items) {
+  const int run = 8 * nqb;
+  const int full = (items / run) * run;
+  int logical = idx;
+  if (idx < full) {
+    const int c = idx / run;
+    const int r = idx - c * run;
+    logical = c * run + (r & 7) * nqb + (r >> 3);
+  }
+  const int g = logical / nqb;
+  const int qb = logical - g * nqb;
+  const int bh_count = B * H;
+  const int fr = g / bh_count;
+  const int bh = g - fr * bh_count;
+  Item it;
+  it.b = bh / H;
+  it.h = bh - it.b * H;
+  it.f = frame_order[fr];
+  it.qb = qb;
+  return it;
+}
+
+struct Workspace {
+  size_t mu, kmax, qmax, bound, elig, qn, qmu, psum, pkmax, pqmax, total;
+};
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int64_t qsb, qss, qsh, ksb, kss, ksh, vsb, vss, vsh, osb, oss, osh;
+  const float* qn;
+  const float* qmu;
+  const float* kmax;
+  const uint8_t* elig;
+  int32_t B, H, S, T, F, w;
+  int32_t gq;     // query granules per item
+  int32_t nqb;    // items per (frame, batch, head)
+  int32_t items;
+  float c;        // scale * log2(e)
+  uint16_t frame_order[kMaxFrameSlots];
+};
+
+struct NormParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t qsb, qss, qsh, ksb, kss, ksh;
+  float* mu;
+  float* kmax;
+  float* qmax;
+  float* bound;
+  uint8_t* elig;
+  float* qn;
+  float* qmu;
+  float* psum;
+  float* pkmax;
+  float* pqmax;
+  int32_t B, H, S, D, nchunk;
+  float scale;
+  float bound_limit;
+};
+
+}  // namespace sfa
+
+struct sfa_plan {
+  sfa_geometry g;
+  float scale;
+  int32_t S;
+  int32_t gq;       // query granules per item (block_q / 16)
+  int32_t nqb;      // T / block_q
+  int32_t items;
+  int32_t nchunk;   // norm-kernel token chunks
+  int64_t active_pairs;
+  sfa::Workspace ws;
+  uint16_t frame_order[sfa::kMaxFrameSlots];
+};
+
+// Launchers (sfa_norms.hip / sfa_fwd.hip); return a hipError_t.
+hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream);
+hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, hipStream_t stream);

@@ -1,0 +1,175 @@
+// Norm array for the Cauchy-Schwarz fixed softmax maximum (gfx950).
+//
+// "HeyGen x Google Cloud: Bringing Avatar IV to TPUs", section "Unchaining
+// softmax" (Fig. 4): a logit is at most ||q|| times the largest key norm;
+// centring the keys on their mean tightens the bound without changing the
+// softmax; heads whose bound is too loose fall back to the online path.
+//
+// Three memory-bound passes, all deterministic (fixed summation order, no
+// atomics). Blocks stream whole token rows ([H, d] contiguous in the usual
+// BSHD layout): thread t owns one 8-element (16-byte) column group of one head.
+//   1. ksum   : per 64-token chunk, column sums of k            -> psum
+//   2. kmean  : mu = (sum over chunks of psum) / S              -> mu
+//   3. stats  : per chunk, max ||k - mu||^2 and max ||q||^2, and per row
+//               ||q|| and <q, mu>                               -> pkmax, pqmax, qn, qmu
+//   4. final  : kmax, qmax, bound = scale * qmax * kmax, eligible = bound <= limit
+#include "sfa_internal.h"
+
+namespace {
+
+using sfa::NormParams;
+using sfa::kNormChunk;
+
+constexpr int kThreads = 256;
+
+__device__ inline void unpack8(const uint4& r, float x[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ inline uint4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Sum over the `lanes` consecutive lanes that share one token row of one head.
+template <int LANES>
+__device__ inline float group_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < LANES; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+__global__ __launch_bounds__(kThreads) void ksum_kernel(NormParams p) {
+  const int chunk = blockIdx.x;
+  const int b = blockIdx.y;
+  const int cpr = p.D / 8;           // column groups per head
+  const int groups = p.H * cpr;
+  const int s0 = chunk * kNormChunk;
+  const int s1 = min(p.S, s0 + kNormChunk);
+  for (int cg = threadIdx.x; cg < groups; cg += kThreads) {
+    const int h = cg / cpr;
+    const int e0 = (cg - h * cpr) * 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const uint16_t* kp = p.k + b * p.ksb + h * p.ksh + e0;
+    for (int s = s0; s < s1; ++s) {
+      float x[8];
+      unpack8(load16(kp + int64_t(s) * p.kss), x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += x[i];
+    }
+    float* out = p.psum + ((int64_t(chunk) * p.B + b) * p.H + h) * p.D + e0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = acc[i];
+  }
+}
+
+__global__ __launch_bounds__(128) void kmean_kernel(NormParams p) {
+  const int bh = blockIdx.x;  // b * H + h
+  const int e = threadIdx.x;
+  if (e >= p.D) return;
+  float acc = 0.f;
+  const int64_t stride = int64_t(p.B) * p.H * p.D;
+  const float* src = p.psum + int64_t(bh) * p.D + e;
+  for (int c = 0; c < p.nchunk; ++c) acc += src[c * stride];
+  p.mu[int64_t(bh) * p.D + e] = acc / float(p.S);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void stats_kernel(NormParams p) {
+  constexpr int CPR = D / 8;  // lanes per (token, head); a power of two <= 16
+  const int chunk = blockIdx.x;
+  const int b = blockIdx.y;
+  const int groups = p.H * CPR;
+  const int s0 = chunk * kNormChunk;
+  const int s1 = min(p.S, s0 + kNormChunk);
+  // groups is a multiple of CPR and the loop stride 256 is too, so the CPR lanes
+  // of one head always iterate together (shuffles stay inside the group)
+  for (int cgb = 0; cgb < groups; cgb += kThreads) {
+    const int cg = cgb + threadIdx.x;
+    const bool active = cg < groups;
+    const int h = active ? cg / CPR : 0;
+    const int e0 = (cg % CPR) * 8;
+    float mu[8];
+    const float* mup = p.mu + (int64_t(b) * p.H + h) * D + e0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mu[i] = active ? mup[i] : 0.f;
+    const uint16_t* kp = p.k + b * p.ksb + h * p.ksh + e0;
+    const uint16_t* qp = p.q + b * p.qsb + h * p.qsh + e0;
+    float kmax2 = 0.f, qmax2 = 0.f;
+    for (int s = s0; s < s1; ++s) {
+      float kx[8], qx[8];
+      if (active) {
+        unpack8(load16(kp + int64_t(s) * p.kss), kx);
+        unpack8(load16(qp + int64_t(s) * p.qss), qx);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kx[i] = qx[i] = 0.f;
+      }
+      float kc = 0.f, qq = 0.f, qm = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float t = kx[i] - mu[i];
+        kc = fmaf(t, t, kc);
+        qq = fmaf(qx[i], qx[i], qq);
+        qm = fmaf(qx[i], mu[i], qm);
+      }
+      kc = group_sum<CPR>(kc);
+      qq = group_sum<CPR>(qq);
+      qm = group_sum<CPR>(qm);
+      kmax2 = fmaxf(kmax2, kc);
+      qmax2 = fmaxf(qmax2, qq);
+      if (active && (cg % CPR) == 0) {
+        const int64_t row = (int64_t(b) * p.H + h) * p.S + s;
+        p.qn[row] = sqrtf(qq);
+        p.qmu[row] = qm;
+      }
+    }
+    if (active && (cg % CPR) == 0) {
+      const int64_t at = (int64_t(chunk) * p.B + b) * p.H + h;
+      p.pkmax[at] = kmax2;
+      p.pqmax[at] = qmax2;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void final_kernel(NormParams p) {
+  const int bh = blockIdx.x * blockDim.x + threadIdx.x;
+  if (bh >= p.B * p.H) return;
+  const int64_t stride = int64_t(p.B) * p.H;
+  float k2 = 0.f, q2 = 0.f;
+  for (int c = 0; c < p.nchunk; ++c) {
+    k2 = fmaxf(k2, p.pkmax[c * stride + bh]);
+    q2 = fmaxf(q2, p.pqmax[c * stride + bh]);
+  }
+  const float kmax = sqrtf(k2);
+  const float qmax = sqrtf(q2);
+  const float bound = p.scale * qmax * kmax;
+  p.kmax[bh] = kmax;
+  p.qmax[bh] = qmax;
+  p.bound[bh] = bound;
+  p.elig[bh] = (p.bound_limit >= 0.f && bound <= p.bound_limit) ? 1 : 0;
+}
+
+}  // namespace
+
+hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream) {
+  const dim3 grid(p.nchunk, p.B);
+  hipLaunchKernelGGL(ksum_kernel, grid, dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kmean_kernel, dim3(p.B * p.H), dim3(128), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.D == 128)
+    hipLaunchKernelGGL(stats_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(stats_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(final_kernel, dim3((p.B * p.H + 255) / 256), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}

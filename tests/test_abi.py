@@ -1,0 +1,179 @@
+"""C-ABI checks that need no GPU: exports, planning, work order and argument errors.
+
+Planning follows "HeyGen x Google Cloud: Bringing Avatar IV to TPUs", section
+"Deleting the mask": query blocks divide the frame span, key ranges are whole
+frames (reference + window), so the plan's ranges expanded to tokens must
+equal the oracle's mask exactly.
+"""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_frame_amd import _lib
+from sparse_attention_frame_amd import workloads as W
+from sparse_attention_frame_amd.api import Plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sfa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sfa_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert sorted(_lib.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (sfa_[a-z_]+)\b", out))
+    assert set(declared) <= exported
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4):
+        assert L.sfa_status_str(st)
+    assert b"unknown" in L.sfa_status_str(7)
+
+
+@pytest.mark.parametrize("name,block_q", [("tiny", 48), ("small", 208), ("720p", 240),
+                                          ("1080p", 240), ("stress", 240)])
+def test_plan_tiles_divide_the_frame(L, name, block_q):
+    wl = W.ALL[name]
+    p = Plan.for_workload(wl)
+    assert p.info["block_q"] == block_q
+    assert wl.tokens_per_frame % p.info["block_q"] == 0 and block_q % 16 == 0
+    assert p.info["granule"] == 16
+    assert p.info["items"] == wl.batch * wl.heads * (wl.frames + 1) * (wl.tokens_per_frame //
+                                                                      block_q)
+
+
+def test_active_pairs_match_oracle_and_golden(L):
+    with open(os.path.join(ROOT, "tests", "golden", "frame_pairs.json")) as f:
+        gold = json.load(f)
+    for name, wl in W.ALL.items():
+        p = Plan.for_workload(wl)
+        T = wl.tokens_per_frame
+        assert p.info["active_pairs"] == gold[name]["pairs"] * T * T * wl.heads * wl.batch
+        assert p.info["active_flops"] == 4.0 * wl.head_dim * p.info["active_pairs"]
+    for wl in (W.TINY, W.SMALL):
+        p = Plan.for_workload(wl)
+        m = oracle.mask_matrix(wl.frames, wl.tokens_per_frame, wl.window)
+        assert p.info["active_pairs"] == int(m.sum()) * wl.heads * wl.batch
+
+
+@pytest.mark.parametrize("F,T,w", [(4, 48, 1), (8, 208, 2), (13, 32, 2), (13, 32, 13), (5, 16, 0),
+                                   (0, 16, 3), (1, 16, 0), (6, 16, 1)])
+def test_key_ranges_expand_to_the_oracle_mask(L, F, T, w):
+    p = Plan(1, 1, 64, F, T, w)
+    mask = oracle.mask_matrix(F, T, w)
+    for f in range(F + 1):
+        ranges = p.key_ranges(f)
+        assert 1 <= len(ranges) <= 2
+        row = np.zeros(mask.shape[1], dtype=bool)
+        for a, b in ranges:
+            assert a % T == 0 and b % T == 0 and a < b
+            row[a:b] = True
+        if len(ranges) == 2:
+            assert ranges[0][1] < ranges[1][0]   # adjacent ranges are merged
+        for i in range(f * T, (f + 1) * T):
+            np.testing.assert_array_equal(mask[i], row)
+
+
+@pytest.mark.parametrize("B,H,F,T,w,bq", [(1, 12, 13, 3600, 2, 0), (2, 3, 4, 48, 1, 16),
+                                          (1, 5, 7, 64, 3, 32), (3, 2, 0, 32, 0, 0),
+                                          (1, 16, 13, 3600, 13, 0)])
+def test_work_items_cover_everything_once_largest_first(L, B, H, F, T, w, bq):
+    p = Plan(B, H, 128, F, T, w, block_q=bq)
+    n = p.info["items"]
+    nqb = T // p.info["block_q"]
+    assert n == B * H * (F + 1) * nqb
+    items = [p.item(i) for i in range(n)]
+    assert len(set(items)) == n
+    for b, h, f, qb in items:
+        assert 0 <= b < B and 0 <= h < H and 0 <= f <= F and 0 <= qb < nqb
+    cost = [len(oracle.key_frames(f, F, w)) for (_, _, f, _) in items]
+    run = 8 * nqb
+    full = n // run * run
+    # whole runs of 8 groups: every run costs no more than the one before
+    for r0 in range(0, full - run, run):
+        assert min(cost[r0:r0 + run]) >= max(cost[r0 + run:r0 + 2 * run])
+        # XCD x (blocks r0 + x, r0 + x + 8, ...) serves one (batch, head, frame) group
+        for x in range(8):
+            assert len({items[i][:3] for i in range(r0 + x, r0 + run, 8)}) == 1
+    assert sorted(cost, reverse=True)[0] == cost[0]
+
+
+def _geom(**kw):
+    g = dict(batch=1, heads=2, head_dim=64, frames=4, tokens_per_frame=48, window=1,
+             scale=0.0, bound_limit=40.0)
+    g.update(kw)
+    return _lib.Geometry(**g)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tokens_per_frame=40), _lib.SFA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), _lib.SFA_ERR_UNSUPPORTED),
+    (dict(window=-1), _lib.SFA_ERR_INVALID),
+    (dict(frames=-1), _lib.SFA_ERR_INVALID),
+    (dict(batch=0), _lib.SFA_ERR_INVALID),
+    (dict(heads=0), _lib.SFA_ERR_INVALID),
+    (dict(scale=-1.0), _lib.SFA_ERR_INVALID),
+    (dict(scale=float("nan")), _lib.SFA_ERR_INVALID),
+    (dict(frames=2000), _lib.SFA_ERR_UNSUPPORTED),
+])
+def test_invalid_geometry(L, kw, status):
+    h = ctypes.c_void_p(123)
+    assert L.sfa_plan_create(ctypes.byref(_geom(**kw)), ctypes.byref(h)) == status
+    assert h.value is None
+
+
+def test_tile_override_errors(L):
+    h = ctypes.c_void_p()
+    g = _geom()
+    for bq in (8, 32, 96, 272, -16):     # not a multiple of 16, not dividing 48, too large
+        assert L.sfa_plan_create_tiled(ctypes.byref(g), bq, ctypes.byref(h)) == \
+            _lib.SFA_ERR_UNSUPPORTED, bq
+    assert L.sfa_plan_create_tiled(ctypes.byref(g), 16, ctypes.byref(h)) == 0
+    L.sfa_plan_destroy(h)
+    assert L.sfa_plan_create(None, ctypes.byref(h)) == _lib.SFA_ERR_INVALID
+    assert L.sfa_plan_create(ctypes.byref(g), None) == _lib.SFA_ERR_INVALID
+
+
+def test_call_validation_happens_before_any_launch(L):
+    """Argument errors are reported without touching the GPU (this runs on CPU)."""
+    p = Plan(1, 2, 64, 4, 48, 1)
+    S = p.seq
+    good = _lib.Tensor(4096, S * 2 * 64, 2 * 64, 64)
+    ws = ctypes.c_void_p(1 << 20)
+    need = p.info["workspace_bytes"]
+    assert L.sfa_norms(p.handle, good, good, None, need, None) == _lib.SFA_ERR_INVALID
+    assert L.sfa_norms(p.handle, good, good, ws, need - 1, None) == _lib.SFA_ERR_INVALID
+    assert L.sfa_norms(None, good, good, ws, need, None) == _lib.SFA_ERR_INVALID
+    bad_ptr = _lib.Tensor(4096 + 8, S * 128, 128, 64)
+    assert L.sfa_norms(p.handle, bad_ptr, good, ws, need, None) == _lib.SFA_ERR_UNSUPPORTED
+    bad_stride = _lib.Tensor(4096, S * 128, 130, 64)
+    assert L.sfa_norms(p.handle, good, bad_stride, ws, need, None) == _lib.SFA_ERR_UNSUPPORTED
+    null_t = _lib.Tensor(None, S * 128, 128, 64)
+    assert L.sfa_fwd(p.handle, good, good, good, null_t, ws, need, None) == _lib.SFA_ERR_INVALID
+    # output aliasing an input is refused
+    assert L.sfa_fwd(p.handle, good, good, good, good, ws, need, None) == _lib.SFA_ERR_INVALID
+    mis_ws = ctypes.c_void_p((1 << 20) + 16)
+    assert L.sfa_fwd(p.handle, good, good, good, _lib.Tensor(1 << 30, S * 128, 128, 64), mis_ws,
+                     need, None) == _lib.SFA_ERR_UNSUPPORTED

@@ -1,0 +1,253 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Tolerance for bf16 inputs with fp32 accumulation: max |O_gpu - O_oracle| <= 2e-2
+and ||O_gpu - O_oracle||_2 / ||O_oracle||_2 <= 5e-3; the per-head eligibility
+flag of the fixed-maximum path must match the oracle exactly.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_frame_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def sfa():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    import sparse_attention_frame_amd as m
+
+    m.lib()  # raises if libsfa.so is missing: no fallback path exists
+    return m
+
+
+def to_dev(*xs):
+    return [torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda() for x in xs]
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = got - ref
+    return float(np.abs(d).max()), float(np.linalg.norm(d) / np.linalg.norm(ref))
+
+
+def assert_close(got, ref, what):
+    mx, rl = errors(got, ref)
+    say(f"  {what}: max_abs={mx:.3e} rel_l2={rl:.3e}")
+    assert mx <= MAX_ABS and rl <= REL_L2, (what, mx, rl)
+
+
+def run(sfa, wl_like, q, k, v, **plan_kw):
+    plan = sfa.Plan(*wl_like, **plan_kw)
+    out, ws = sfa.attention(plan, q, k, v)
+    torch.cuda.synchronize()
+    return plan, out, ws
+
+
+def geom(wl):
+    return (wl.batch, wl.heads, wl.head_dim, wl.frames, wl.tokens_per_frame, wl.window)
+
+
+def check_stats(sfa, plan, ws, q_np, k_np, bound_limit=40.0):
+    st = sfa.head_stats(plan, ws)
+    ref = oracle.head_stats(q_np, k_np, bound_limit=bound_limit)
+    np.testing.assert_array_equal(st["eligible"], ref["eligible"])
+    np.testing.assert_allclose(st["kmax"], ref["kmax"], rtol=1e-4)
+    np.testing.assert_allclose(st["qmax"], ref["qmax"], rtol=1e-5)
+    np.testing.assert_allclose(st["bound"], ref["bound"], rtol=1e-4)
+    np.testing.assert_allclose(st["mu"], ref["mu"], rtol=0, atol=1e-4 * (1 + np.abs(ref["mu"]).max()))
+    return st, ref
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_parity_full(sfa, name):
+    wl = W.ALL[name]
+    say(f"[parity_full] {name}")
+    q_np, k_np, v_np = W.make_inputs_np(wl)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    plan, out, ws = run(sfa, geom(wl), q, k, v)
+    ref = oracle.attention(q_np, k_np, v_np, wl.frames, wl.tokens_per_frame, wl.window)
+    assert_close(out.float().cpu().numpy(), ref, name)
+    st, ref_st = check_stats(sfa, plan, ws, q_np, k_np)
+    assert st["eligible"].all()
+    # per-row half of the norm array
+    qn, qmu = sfa.row_norms(plan, ws)
+    qd = q_np.astype(np.float64)
+    np.testing.assert_allclose(qn, np.sqrt((qd ** 2).sum(-1)).transpose(0, 2, 1), rtol=1e-5)
+    np.testing.assert_allclose(qmu, np.einsum("bshd,bhd->bhs", qd, ref_st["mu"]), rtol=0,
+                               atol=1e-3)
+
+
+def sample_rows(wl, n_random=24, seed=0):
+    T, S = wl.tokens_per_frame, wl.seq
+    rows = set()
+    for f in range(wl.frames + 1):
+        rows.update({f * T, f * T + 15, f * T + 16, f * T + T // 2, (f + 1) * T - 1})
+    g = np.random.default_rng(seed)
+    rows.update(int(x) for x in g.integers(0, S, n_random))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["720p", "1080p", "stress", "stress_w13"])
+def test_parity_sampled_full_size(sfa, name):
+    """Full-size inputs in the benchmark's launch configuration; sampled rows of every head."""
+    wl = W.ALL[name]
+    say(f"[parity_sampled] {name} generating inputs")
+    q_np, k_np, v_np = W.make_inputs_np(wl)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    say(f"[parity_sampled] {name} launching")
+    plan, out, ws = run(sfa, geom(wl), q, k, v)
+    st, _ = check_stats(sfa, plan, ws, q_np, k_np)
+    expect_bad = set(wl.boost_heads)
+    assert {h for h in range(wl.heads) if not st["eligible"][0, h]} == expect_bad
+    rows = sample_rows(wl)
+    got_all = out[0, torch.from_numpy(rows).cuda()].float().cpu().numpy()   # [R, H, d]
+    for h in range(wl.heads):
+        ref = oracle.attention_rows(q_np, k_np, v_np, wl.frames, wl.tokens_per_frame, wl.window,
+                                    0, h, rows)
+        assert_close(got_all[:, h], ref, f"{name} head {h} ({len(rows)} rows)")
+    assert torch.isfinite(out.float()).all()
+
+
+def test_full_size_frame_indicator_has_no_mass_outside_window(sfa):
+    """720p shape, every row: with v_j = one-hot(frame(j)) the output is exactly zero on
+    frames outside the row's window and sums to ~1 (any size, no oracle needed)."""
+    wl = W.P720
+    say("[frame_indicator] 720p")
+    q_np, k_np, _ = W.make_inputs_np(wl)
+    q, k = to_dev(q_np, k_np)
+    T, F = wl.tokens_per_frame, wl.frames
+    v = torch.zeros_like(q)
+    frame = torch.arange(wl.seq, device="cuda") // T
+    v[0, torch.arange(wl.seq, device="cuda"), :, frame] = 1.0
+    plan, out, _ = run(sfa, geom(wl), q, k, v)
+    o = out[0, :, :, :F + 1].float()                               # [S, H, F+1]
+    allowed = torch.from_numpy(oracle.mask_matrix(F, 1, wl.window)).cuda()  # frame level
+    outside = ~allowed[frame]                                      # [S, F+1]
+    assert (o[outside.unsqueeze(1).expand_as(o)] == 0).all()
+    assert (o[(~outside).unsqueeze(1).expand_as(o)] > 0).all()
+    assert torch.allclose(o.sum(-1), torch.ones_like(o[..., 0]), atol=1e-2)
+    assert (out[0, :, :, F + 1:] == 0).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_forced_online_path(sfa, name):
+    wl = W.ALL[name]
+    say(f"[forced_online] {name}")
+    q_np, k_np, v_np = W.make_inputs_np(wl)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    plan, out, ws = run(sfa, geom(wl), q, k, v, bound_limit=-1.0)
+    st = sfa.head_stats(plan, ws)
+    assert not st["eligible"].any()
+    ref = oracle.attention(q_np, k_np, v_np, wl.frames, wl.tokens_per_frame, wl.window)
+    assert_close(out.float().cpu().numpy(), ref, f"{name} online")
+
+
+# (F, T, w, H, d, B): tails of 1, 2 and 3 granules, a lone granule, reference frame only,
+# window 0, window past both ends, batch 2, d = 64 and 128, 5-granule query blocks
+RAGGED = [(0, 16, 0, 1, 64, 1), (1, 16, 0, 2, 128, 1), (2, 48, 1, 2, 64, 2), (3, 80, 5, 3, 128, 1),
+          (6, 48, 1, 2, 128, 1), (5, 32, 2, 1, 64, 1), (4, 112, 1, 2, 128, 2), (9, 16, 3, 4, 128, 1)]
+
+
+@pytest.mark.parametrize("F,T,w,H,d,B", RAGGED)
+@pytest.mark.parametrize("limit", [40.0, -1.0])
+def test_ragged_geometries(sfa, F, T, w, H, d, B, limit):
+    say(f"[ragged] F={F} T={T} w={w} H={H} d={d} B={B} limit={limit}")
+    S = (F + 1) * T
+    g = np.random.default_rng(F * 1000 + T + w)
+    q_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    k_np = (g.standard_normal((B, S, H, d)) + 3 * g.standard_normal((B, 1, H, d))).astype(
+        np.float32)
+    v_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
+    plan, out, ws = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit)
+    ref = oracle.attention(q_np, k_np, v_np, F, T, w)
+    assert_close(out.float().cpu().numpy(), ref, "ragged")
+    check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
+
+
+def test_zero_query_gives_window_mean(sfa):
+    F, T, w, H, d = 6, 48, 1, 2, 128
+    say("[zero_query]")
+    S = (F + 1) * T
+    g = np.random.default_rng(3)
+    v_np = g.standard_normal((1, S, H, d)).astype(np.float32)
+    k_np = g.standard_normal((1, S, H, d)).astype(np.float32)
+    q, k, v = to_dev(np.zeros_like(v_np), k_np, v_np)
+    plan, out, _ = run(sfa, (1, H, d, F, T, w), q, k, v)
+    vv = v.float().cpu().numpy().astype(np.float64)
+    got = out.float().cpu().numpy()
+    for f in range(F + 1):
+        frames = [0] if f == 0 else [0] + [x for x in range(f - w, f + w + 1) if 1 <= x <= F]
+        mean = np.mean(np.concatenate([vv[0, x * T:(x + 1) * T] for x in frames]), axis=0)
+        assert_close(got[0, f * T:(f + 1) * T], np.broadcast_to(mean, (T, H, d)), f"frame {f}")
+
+
+def test_double_run_is_bitwise_identical(sfa):
+    """Two runs of one build must agree bit for bit before differences are trusted."""
+    wl = W.SMALL
+    say("[determinism] small")
+    q, k, v = to_dev(*W.make_inputs_np(wl))
+    _, a, wa = run(sfa, geom(wl), q, k, v)
+    _, b, wb = run(sfa, geom(wl), q, k, v)
+    assert torch.equal(a, b)
+    # the defined parts of the workspace (sections are padded to 256 bytes)
+    pa = sfa.Plan(*geom(wl))
+    sa, sb = sfa.head_stats(pa, wa), sfa.head_stats(pa, wb)
+    for key in sa:
+        np.testing.assert_array_equal(sa[key], sb[key])
+    for x, y in zip(sfa.row_norms(pa, wa), sfa.row_norms(pa, wb)):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_head_subset_and_layouts_are_bitwise_equal(sfa):
+    """Head groups see exactly the same mask; strided layouts change nothing."""
+    wl = W.SMALL
+    say("[layouts] small")
+    q, k, v = to_dev(*W.make_inputs_np(wl))
+    _, full, _ = run(sfa, geom(wl), q, k, v)
+    # a group of heads as strided views of the full tensors
+    sub = (wl.batch, 3, wl.head_dim, wl.frames, wl.tokens_per_frame, wl.window)
+    _, part, _ = run(sfa, sub, q[:, :, 2:5], k[:, :, 2:5], v[:, :, 2:5])
+    assert torch.equal(part, full[:, :, 2:5])
+    # BHSD storage viewed as [B, S, H, d]
+    qh, kh, vh = (x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for x in (q, k, v))
+    assert qh.stride(2) == wl.seq * wl.head_dim
+    plan = sfa.Plan(*geom(wl))
+    ws = plan.workspace()
+    outh = torch.empty_like(qh)
+    sfa.attention(plan, qh, kh, vh, out=outh, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(outh, full)
+
+
+def test_error_paths_on_device(sfa):
+    wl = W.TINY
+    q, k, v = to_dev(*W.make_inputs_np(wl))
+    plan = sfa.Plan(*geom(wl))
+    bad = torch.empty(q.numel() + 8, dtype=torch.bfloat16, device="cuda")[4:4 + q.numel()]
+    bad = bad.view(q.shape)
+    with pytest.raises(sfa.SfaError) as e:
+        sfa.attention(plan, bad, k, v)
+    assert e.value.status == -2
+    small_ws = torch.empty(plan.info["workspace_bytes"] - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sfa.SfaError) as e:
+        sfa.attention(plan, q, k, v, workspace=small_ws)
+    assert e.value.status == -1
+    with pytest.raises(ValueError):
+        sfa.attention(plan, q[:, :-16], k, v)
