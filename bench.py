@@ -65,6 +65,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--waves", type=int, default=0, help="override waves per workgroup (4 or 8)")
+    ap.add_argument("--block-q", type=int, default=0, help="override query rows per work item")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -82,7 +84,7 @@ def main():
     q_np, k_np, v_np = W.make_inputs_np(wl)
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q_np, k_np, v_np))
-    plan = sfa.Plan.for_workload(wl)
+    plan = sfa.Plan.for_workload(wl, waves=args.waves, block_q=args.block_q)
     ws = plan.workspace(dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
@@ -141,14 +143,15 @@ def main():
         "config": {"workload": f"{wl.name}-shaped layer: reference frame + F={wl.frames} frames x "
                                f"T={wl.tokens_per_frame} tokens (S={wl.seq}), H={wl.heads}, "
                                f"d={wl.head_dim}, window +-{wl.window}, batch {wl.batch}",
-                   "block_q": info["block_q"], "items": info["items"],
+                   "block_q": info["block_q"], "waves": info["waves_per_item"],
+                   "items": info["items"],
                    "active_gflop": round(flops / 1e9, 1),
                    "eligible_heads": int(st["eligible"].sum()), "heads": wl.heads},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_ms, 4),
         "fwd_min_ms": round(fwd_min, 4),
         "norms_ms": round(norms_ms, 4),
-        "roofline": {"bound": "mfma", "kernel": "fwd_kernel<128>",
+        "roofline": {"bound": "mfma", "kernel": "fwd_kernel",
                      "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},

@@ -21,7 +21,7 @@
  *   - device pointers (tensor data, workspace) are owned by the caller; the
  *     library never allocates or frees device memory;
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); work
- *     is enqueued asynchronously on it; only sfa_read_head_stats synchronises;
+ *     is enqueued asynchronously on it; only the sfa_read_* calls synchronise;
  *   - a plan owns host memory only, is immutable after creation and may be
  *     shared by threads.
  */
@@ -82,9 +82,18 @@ typedef struct sfa_plan_info {
  * call, no device memory). *out is set to NULL on error. */
 int sfa_plan_create(const sfa_geometry* geom, sfa_plan** out);
 
-/* Same, forcing the query rows per work item (0 = automatic). block_q must be a
- * multiple of 16 that divides T and is at most 256 (else SFA_ERR_UNSUPPORTED). */
-int sfa_plan_create_tiled(const sfa_geometry* geom, int32_t block_q, sfa_plan** out);
+/* Tuning overrides for sfa_plan_create_ex; 0 in a field selects the default. */
+typedef struct sfa_plan_options {
+  int32_t block_q;        /* query rows per work item: a multiple of 16 that divides T,
+                             at most 256 (default: the largest such divisor) */
+  int32_t waves_per_item; /* 8 (default: 32 query rows per wave, two waves per SIMD)
+                             or 4 (64 rows per wave, one wave per SIMD) */
+} sfa_plan_options;
+
+/* sfa_plan_create with overrides (options may be NULL). Values outside the
+ * ranges above give SFA_ERR_UNSUPPORTED. */
+int sfa_plan_create_ex(const sfa_geometry* geom, const sfa_plan_options* options,
+                       sfa_plan** out);
 
 void sfa_plan_destroy(sfa_plan* plan);
 

@@ -26,6 +26,10 @@ class Tensor(ctypes.Structure):
                 ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
 
 
+class PlanOptions(ctypes.Structure):
+    _fields_ = [("block_q", ctypes.c_int32), ("waves_per_item", ctypes.c_int32)]
+
+
 class PlanInfo(ctypes.Structure):
     _fields_ = [("block_q", ctypes.c_int32), ("granule", ctypes.c_int32),
                 ("waves_per_item", ctypes.c_int32), ("items", ctypes.c_int32),
@@ -35,7 +39,7 @@ class PlanInfo(ctypes.Structure):
 
 # every symbol include/sfa.h declares
 EXPORTS = (
-    "sfa_plan_create", "sfa_plan_create_tiled", "sfa_plan_destroy", "sfa_plan_get_info",
+    "sfa_plan_create", "sfa_plan_create_ex", "sfa_plan_destroy", "sfa_plan_get_info",
     "sfa_plan_key_ranges", "sfa_plan_item", "sfa_norms", "sfa_fwd", "sfa_attention",
     "sfa_read_head_stats", "sfa_read_row_norms", "sfa_status_str",
 )
@@ -57,8 +61,8 @@ def _declare(lib):
     u8p = ctypes.POINTER(ctypes.c_uint8)
     sigs = {
         "sfa_plan_create": (ctypes.c_int, [ctypes.POINTER(Geometry), ctypes.POINTER(P)]),
-        "sfa_plan_create_tiled": (ctypes.c_int, [ctypes.POINTER(Geometry), ctypes.c_int32,
-                                                 ctypes.POINTER(P)]),
+        "sfa_plan_create_ex": (ctypes.c_int, [ctypes.POINTER(Geometry),
+                                              ctypes.POINTER(PlanOptions), ctypes.POINTER(P)]),
         "sfa_plan_destroy": (None, [P]),
         "sfa_plan_get_info": (ctypes.c_int, [P, ctypes.POINTER(PlanInfo)]),
         "sfa_plan_key_ranges": (ctypes.c_int, [P, ctypes.c_int32, i32p, i32p]),

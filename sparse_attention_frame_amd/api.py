@@ -13,7 +13,7 @@ import ctypes
 import numpy as np
 
 from . import _lib
-from ._lib import Geometry, PlanInfo, Tensor, check, lib
+from ._lib import Geometry, PlanInfo, PlanOptions, Tensor, check, lib
 
 
 def _stream_ptr(stream):
@@ -29,14 +29,15 @@ class Plan:
 
     def __init__(self, batch: int, heads: int, head_dim: int, frames: int,
                  tokens_per_frame: int, window: int, scale: float = 0.0,
-                 bound_limit: float = 40.0, block_q: int = 0):
+                 bound_limit: float = 40.0, block_q: int = 0, waves: int = 0):
         self.geometry = Geometry(batch, heads, head_dim, frames, tokens_per_frame, window,
                                  scale, bound_limit)
         handle = ctypes.c_void_p()
         L = lib()
-        if block_q:
-            st = L.sfa_plan_create_tiled(ctypes.byref(self.geometry), block_q,
-                                         ctypes.byref(handle))
+        if block_q or waves:
+            opts = PlanOptions(block_q, waves)
+            st = L.sfa_plan_create_ex(ctypes.byref(self.geometry), ctypes.byref(opts),
+                                      ctypes.byref(handle))
         else:
             st = L.sfa_plan_create(ctypes.byref(self.geometry), ctypes.byref(handle))
         check(st, "sfa_plan_create")

@@ -46,20 +46,23 @@ int validate_geometry(const sfa_geometry* g) {
 }
 
 // Query granules per work item: the largest divisor of T/16 that fits one
-// workgroup (4 waves x 4 sub-tiles of 16 rows).
+// workgroup (8 query tiles of 32 rows).
 int auto_block_granules(int t_granules) {
   for (int g = kMaxBlockGranules; g >= 1; --g)
     if (t_granules % g == 0) return g;
   return 1;
 }
 
-int create(const sfa_geometry* geom, int32_t block_q, sfa_plan** out) {
+int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out) {
   if (!out) return SFA_ERR_INVALID;
   *out = nullptr;
   int st = validate_geometry(geom);
   if (st != SFA_OK) return st;
   const int T = geom->tokens_per_frame;
   const int tg = T / kGranule;
+  const int block_q = opt ? opt->block_q : 0;
+  const int waves = (opt && opt->waves_per_item) ? opt->waves_per_item : 8;
+  if (waves != 4 && waves != 8) return SFA_ERR_UNSUPPORTED;
   int gq;
   if (block_q == 0) {
     gq = auto_block_granules(tg);
@@ -78,6 +81,7 @@ int create(const sfa_geometry* geom, int32_t block_q, sfa_plan** out) {
   p->scale = geom->scale == 0.0f ? 1.0f / sqrtf(float(D)) : geom->scale;
   p->S = (F + 1) * T;
   p->gq = gq;
+  p->waves = waves;
   p->nqb = tg / gq;
   p->items = B * H * (F + 1) * p->nqb;
   p->nchunk = (p->S + kNormChunk - 1) / kNormChunk;
@@ -164,10 +168,13 @@ NormParams norm_params(const sfa_plan* p, const sfa_tensor& q, const sfa_tensor&
 
 extern "C" {
 
-int sfa_plan_create(const sfa_geometry* geom, sfa_plan** out) { return create(geom, 0, out); }
+int sfa_plan_create(const sfa_geometry* geom, sfa_plan** out) {
+  return create(geom, nullptr, out);
+}
 
-int sfa_plan_create_tiled(const sfa_geometry* geom, int32_t block_q, sfa_plan** out) {
-  return create(geom, block_q, out);
+int sfa_plan_create_ex(const sfa_geometry* geom, const sfa_plan_options* options,
+                       sfa_plan** out) {
+  return create(geom, options, out);
 }
 
 void sfa_plan_destroy(sfa_plan* plan) { delete plan; }
@@ -176,7 +183,7 @@ int sfa_plan_get_info(const sfa_plan* p, sfa_plan_info* out) {
   if (!p || !out) return SFA_ERR_INVALID;
   out->block_q = p->gq * kGranule;
   out->granule = kGranule;
-  out->waves_per_item = kFwdWaves;
+  out->waves_per_item = p->waves;
   out->items = p->items;
   out->active_pairs = p->active_pairs;
   out->active_flops = 4.0 * p->g.head_dim * double(p->active_pairs);
@@ -255,7 +262,8 @@ int sfa_fwd(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_ten
   f.gq = p->gq; f.nqb = p->nqb; f.items = p->items;
   f.c = p->scale * 1.4426950408889634f;
   memcpy(f.frame_order, p->frame_order, sizeof(f.frame_order));
-  return hip_status(sfa_launch_fwd(f, p->g.head_dim, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      sfa_launch_fwd(f, p->g.head_dim, p->waves, static_cast<hipStream_t>(stream)));
 }
 
 int sfa_attention(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_tensor o,

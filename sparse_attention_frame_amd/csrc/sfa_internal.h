@@ -11,9 +11,7 @@ namespace sfa {
 
 constexpr int kGranule = 16;       // token granule: finest bf16 row tiling of the MFMA
 constexpr int kMaxFrameSlots = 1024;  // F + 1 limit (frame order table travels in kernel args)
-constexpr int kFwdWaves = 4;       // waves per attention workgroup
-constexpr int kFwdSub = 4;         // 16-row query sub-tiles per wave
-constexpr int kMaxBlockGranules = kFwdWaves * kFwdSub;  // <= 256 query rows per item
+constexpr int kMaxBlockGranules = 16;  // <= 256 query rows per item (8 tiles of 32)
 constexpr int kNormChunk = 64;     // tokens per block in the norm kernels
 
 // Visible key ranges of one query frame: [0, r0_end) and [r1_begin, r1_end)
@@ -134,6 +132,7 @@ struct sfa_plan {
   float scale;
   int32_t S;
   int32_t gq;       // query granules per item (block_q / 16)
+  int32_t waves;    // waves per attention workgroup (4 or 8)
   int32_t nqb;      // T / block_q
   int32_t items;
   int32_t nchunk;   // norm-kernel token chunks
@@ -144,4 +143,4 @@ struct sfa_plan {
 
 // Launchers (sfa_norms.hip / sfa_fwd.hip); return a hipError_t.
 hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream);
-hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, hipStream_t stream);
+hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, int waves, hipStream_t stream);

@@ -67,15 +67,33 @@ __global__ __launch_bounds__(kThreads) void ksum_kernel(NormParams p) {
   }
 }
 
-__global__ __launch_bounds__(128) void kmean_kernel(NormParams p) {
+// mu = (sum of the chunk partials) / S. One block per (b, h): D columns x P
+// parts; part j adds chunks j, j+P, ... in order, then the parts are added in
+// a fixed order.
+constexpr int kReduceThreads = 1024;
+
+__global__ __launch_bounds__(kReduceThreads) void kmean_kernel(NormParams p) {
+  __shared__ float part[kReduceThreads];
   const int bh = blockIdx.x;  // b * H + h
-  const int e = threadIdx.x;
-  if (e >= p.D) return;
-  float acc = 0.f;
+  const int e = threadIdx.x % p.D;
+  const int j = threadIdx.x / p.D;
+  const int parts = kReduceThreads / p.D;
   const int64_t stride = int64_t(p.B) * p.H * p.D;
   const float* src = p.psum + int64_t(bh) * p.D + e;
-  for (int c = 0; c < p.nchunk; ++c) acc += src[c * stride];
-  p.mu[int64_t(bh) * p.D + e] = acc / float(p.S);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int c = j;
+  for (; c + 3 * parts < p.nchunk; c += 4 * parts) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += src[(c + u * parts) * stride];
+  }
+  for (; c < p.nchunk; c += parts) acc[0] += src[c * stride];
+  part[threadIdx.x] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (j == 0) {
+    float t = 0.f;
+    for (int q = 0; q < parts; ++q) t += part[q * p.D + e];
+    p.mu[int64_t(bh) * p.D + e] = t / float(p.S);
+  }
 }
 
 template <int D>
@@ -136,22 +154,36 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(NormParams p) {
   }
 }
 
+// Per (b, h): kmax, qmax (max over the chunk partials of squared norms), the
+// bound and the eligibility flag. One block per (b, h).
 __global__ __launch_bounds__(256) void final_kernel(NormParams p) {
-  const int bh = blockIdx.x * blockDim.x + threadIdx.x;
-  if (bh >= p.B * p.H) return;
+  __shared__ float k2s[256], q2s[256];
+  const int bh = blockIdx.x;
   const int64_t stride = int64_t(p.B) * p.H;
   float k2 = 0.f, q2 = 0.f;
-  for (int c = 0; c < p.nchunk; ++c) {
+  for (int c = threadIdx.x; c < p.nchunk; c += 256) {
     k2 = fmaxf(k2, p.pkmax[c * stride + bh]);
     q2 = fmaxf(q2, p.pqmax[c * stride + bh]);
   }
-  const float kmax = sqrtf(k2);
-  const float qmax = sqrtf(q2);
-  const float bound = p.scale * qmax * kmax;
-  p.kmax[bh] = kmax;
-  p.qmax[bh] = qmax;
-  p.bound[bh] = bound;
-  p.elig[bh] = (p.bound_limit >= 0.f && bound <= p.bound_limit) ? 1 : 0;
+  k2s[threadIdx.x] = k2;
+  q2s[threadIdx.x] = q2;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      k2s[threadIdx.x] = fmaxf(k2s[threadIdx.x], k2s[threadIdx.x + w]);
+      q2s[threadIdx.x] = fmaxf(q2s[threadIdx.x], q2s[threadIdx.x + w]);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float kmax = sqrtf(k2s[0]);
+    const float qmax = sqrtf(q2s[0]);
+    const float bound = p.scale * qmax * kmax;
+    p.kmax[bh] = kmax;
+    p.qmax[bh] = qmax;
+    p.bound[bh] = bound;
+    p.elig[bh] = (p.bound_limit >= 0.f && bound <= p.bound_limit) ? 1 : 0;
+  }
 }
 
 }  // namespace
@@ -161,7 +193,7 @@ hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(ksum_kernel, grid, dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kmean_kernel, dim3(p.B * p.H), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL(kmean_kernel, dim3(p.B * p.H), dim3(kReduceThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.D == 128)
@@ -170,6 +202,6 @@ hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(stats_kernel<64>, grid, dim3(kThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(final_kernel, dim3((p.B * p.H + 255) / 256), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(final_kernel, dim3(p.B * p.H), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -148,9 +148,21 @@ def test_tile_override_errors(L):
     h = ctypes.c_void_p()
     g = _geom()
     for bq in (8, 32, 96, 272, -16):     # not a multiple of 16, not dividing 48, too large
-        assert L.sfa_plan_create_tiled(ctypes.byref(g), bq, ctypes.byref(h)) == \
+        opt = _lib.PlanOptions(bq, 0)
+        assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == \
             _lib.SFA_ERR_UNSUPPORTED, bq
-    assert L.sfa_plan_create_tiled(ctypes.byref(g), 16, ctypes.byref(h)) == 0
+    for waves in (1, 2, 6, 16, -4):
+        opt = _lib.PlanOptions(0, waves)
+        assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == \
+            _lib.SFA_ERR_UNSUPPORTED, waves
+    for bq, waves in ((16, 0), (48, 4), (0, 8)):
+        opt = _lib.PlanOptions(bq, waves)
+        assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == 0
+        info = _lib.PlanInfo()
+        assert L.sfa_plan_get_info(h, ctypes.byref(info)) == 0
+        assert info.block_q == (bq or 48) and info.waves_per_item == (waves or 8)
+        L.sfa_plan_destroy(h)
+    assert L.sfa_plan_create_ex(ctypes.byref(g), None, ctypes.byref(h)) == 0
     L.sfa_plan_destroy(h)
     assert L.sfa_plan_create(None, ctypes.byref(h)) == _lib.SFA_ERR_INVALID
     assert L.sfa_plan_create(ctypes.byref(g), None) == _lib.SFA_ERR_INVALID
