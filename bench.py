@@ -67,6 +67,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--waves", type=int, default=0, help="override waves per workgroup (4 or 8)")
     ap.add_argument("--block-q", type=int, default=0, help="override query rows per work item")
+    ap.add_argument("--lds-stages", type=int, default=0, help="override K/V stages in flight")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one elementwise copy of this size (calibrates HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -84,7 +87,8 @@ def main():
     q_np, k_np, v_np = W.make_inputs_np(wl)
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q_np, k_np, v_np))
-    plan = sfa.Plan.for_workload(wl, waves=args.waves, block_q=args.block_q)
+    plan = sfa.Plan.for_workload(wl, waves=args.waves, block_q=args.block_q,
+                                 lds_stages=args.lds_stages)
     ws = plan.workspace(dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
@@ -156,6 +160,13 @@ def main():
                      "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 2
+        x = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        y = torch.empty_like(x)
+        torch.neg(x, out=y)          # reads and writes exactly copy_probe_mib MiB
+        torch.cuda.synchronize()
+        res["copy_probe_mib"] = args.copy_probe_mib
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(wl, q_np, k_np, v_np)

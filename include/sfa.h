@@ -57,7 +57,8 @@ typedef struct sfa_geometry {
 
 /* A bf16 tensor [B, S, H, d] addressed as
  * data + b*stride_b + s*stride_s + h*stride_h + e  (strides in elements, d contiguous).
- * data must be 16-byte aligned and every stride a multiple of 8. */
+ * data must be 16-byte aligned, every stride a multiple of 8 and stride_s at
+ * most 2^24 (SFA_ERR_UNSUPPORTED otherwise). */
 typedef struct sfa_tensor {
   void* data;
   int64_t stride_b;
@@ -88,6 +89,8 @@ typedef struct sfa_plan_options {
                              at most 256 (default: the largest such divisor) */
   int32_t waves_per_item; /* 8 (default: 32 query rows per wave, two waves per SIMD)
                              or 4 (64 rows per wave, one wave per SIMD) */
+  int32_t lds_stages;     /* 64-key K/V stages in LDS: 2, 3 or 4 (default 3, which
+                             selects the software-pipelined loop of the 8-wave kernel) */
 } sfa_plan_options;
 
 /* sfa_plan_create with overrides (options may be NULL). Values outside the
@@ -120,10 +123,12 @@ int sfa_plan_item(const sfa_plan* plan, int32_t index, int32_t item[4]);
 int sfa_norms(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, void* workspace,
               size_t workspace_bytes, void* stream);
 
-/* The attention kernel: one pass over each query block's reference-frame and
- * window key granules, fixed maximum for eligible heads, online softmax for the
- * others. Requires sfa_norms to have run on the same q, k and workspace earlier
- * on the stream. o may not alias q, k or v. */
+/* The attention: a memory-bound pass stages V^T [b][h][d][S] in the workspace,
+ * then the attention kernel makes one pass over each query block's
+ * reference-frame and window key granules, with the fixed maximum for eligible
+ * heads and the online softmax for the others. Requires sfa_norms to have run
+ * on the same q, k and workspace earlier on the stream. o may not alias q, k
+ * or v. */
 int sfa_fwd(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_tensor o,
             void* workspace, size_t workspace_bytes, void* stream);
 

@@ -27,7 +27,8 @@ class Tensor(ctypes.Structure):
 
 
 class PlanOptions(ctypes.Structure):
-    _fields_ = [("block_q", ctypes.c_int32), ("waves_per_item", ctypes.c_int32)]
+    _fields_ = [("block_q", ctypes.c_int32), ("waves_per_item", ctypes.c_int32),
+                ("lds_stages", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):

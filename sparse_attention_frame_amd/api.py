@@ -29,13 +29,14 @@ class Plan:
 
     def __init__(self, batch: int, heads: int, head_dim: int, frames: int,
                  tokens_per_frame: int, window: int, scale: float = 0.0,
-                 bound_limit: float = 40.0, block_q: int = 0, waves: int = 0):
+                 bound_limit: float = 40.0, block_q: int = 0, waves: int = 0,
+                 lds_stages: int = 0):
         self.geometry = Geometry(batch, heads, head_dim, frames, tokens_per_frame, window,
                                  scale, bound_limit)
         handle = ctypes.c_void_p()
         L = lib()
-        if block_q or waves:
-            opts = PlanOptions(block_q, waves)
+        if block_q or waves or lds_stages:
+            opts = PlanOptions(block_q, waves, lds_stages)
             st = L.sfa_plan_create_ex(ctypes.byref(self.geometry), ctypes.byref(opts),
                                       ctypes.byref(handle))
         else:

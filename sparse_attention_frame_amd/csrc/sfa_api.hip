@@ -40,8 +40,10 @@ int validate_geometry(const sfa_geometry* g) {
   if (g->tokens_per_frame % kGranule != 0) return SFA_ERR_UNSUPPORTED;
   if (g->frames + 1 > kMaxFrameSlots) return SFA_ERR_UNSUPPORTED;
   const int64_t S = int64_t(g->frames + 1) * g->tokens_per_frame;
-  // 32-bit token and row indices inside the kernels
+  // 32-bit token and row indices inside the kernels; one head's V^T (d x S bf16)
+  // is addressed with 32-bit byte offsets
   if (S * g->heads * int64_t(g->batch) > (int64_t(1) << 31) - 1) return SFA_ERR_UNSUPPORTED;
+  if (S * g->head_dim * 2 > (int64_t(1) << 31) - 1) return SFA_ERR_UNSUPPORTED;
   return SFA_OK;
 }
 
@@ -63,6 +65,8 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   const int block_q = opt ? opt->block_q : 0;
   const int waves = (opt && opt->waves_per_item) ? opt->waves_per_item : 8;
   if (waves != 4 && waves != 8) return SFA_ERR_UNSUPPORTED;
+  const int stages = (opt && opt->lds_stages) ? opt->lds_stages : 3;
+  if (stages < 2 || stages > 4) return SFA_ERR_UNSUPPORTED;
   int gq;
   if (block_q == 0) {
     gq = auto_block_granules(tg);
@@ -82,6 +86,7 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   p->S = (F + 1) * T;
   p->gq = gq;
   p->waves = waves;
+  p->stages = stages;
   p->nqb = tg / gq;
   p->items = B * H * (F + 1) * p->nqb;
   p->nchunk = (p->S + kNormChunk - 1) / kNormChunk;
@@ -113,6 +118,7 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   p->ws.psum = take(size_t(p->nchunk) * bh * D * 4);  // [chunk][b][h][d]
   p->ws.pkmax = take(size_t(p->nchunk) * bh * 4);     // [chunk][b][h], squared norms
   p->ws.pqmax = take(size_t(p->nchunk) * bh * 4);
+  p->ws.vt = take(bh * size_t(D) * size_t(p->S) * 2);  // bf16 V^T [b][h][d][S]
   p->ws.total = off;
   *out = p;
   return SFA_OK;
@@ -123,6 +129,8 @@ int check_tensor(const sfa_tensor& t) {
   if (t.stride_b < 0 || t.stride_s < 0 || t.stride_h < 0) return SFA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(t.data) & 15) != 0) return SFA_ERR_UNSUPPORTED;
   if ((t.stride_b | t.stride_s | t.stride_h) & 7) return SFA_ERR_UNSUPPORTED;
+  // the kernels address 64 rows of one head with 32-bit byte offsets
+  if (t.stride_s > (int64_t(1) << 24)) return SFA_ERR_UNSUPPORTED;
   return SFA_OK;
 }
 
@@ -257,13 +265,14 @@ int sfa_fwd(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_ten
   f.qmu = reinterpret_cast<const float*>(base + p->ws.qmu);
   f.kmax = reinterpret_cast<const float*>(base + p->ws.kmax);
   f.elig = reinterpret_cast<const uint8_t*>(base + p->ws.elig);
+  f.vt = reinterpret_cast<uint16_t*>(base + p->ws.vt);
   f.B = p->g.batch; f.H = p->g.heads; f.S = p->S; f.T = p->g.tokens_per_frame;
   f.F = p->g.frames; f.w = p->g.window;
   f.gq = p->gq; f.nqb = p->nqb; f.items = p->items;
   f.c = p->scale * 1.4426950408889634f;
   memcpy(f.frame_order, p->frame_order, sizeof(f.frame_order));
   return hip_status(
-      sfa_launch_fwd(f, p->g.head_dim, p->waves, static_cast<hipStream_t>(stream)));
+      sfa_launch_fwd(f, p->g.head_dim, p->waves, p->stages, static_cast<hipStream_t>(stream)));
 }
 
 int sfa_attention(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_tensor o,

@@ -85,7 +85,7 @@ __host__ __device__ inline Item decode_item(int idx, const uint16_t* frame_order
 }
 
 struct Workspace {
-  size_t mu, kmax, qmax, bound, elig, qn, qmu, psum, pkmax, pqmax, total;
+  size_t mu, kmax, qmax, bound, elig, qn, qmu, psum, pkmax, pqmax, vt, total;
 };
 
 struct FwdParams {
@@ -98,6 +98,7 @@ struct FwdParams {
   const float* qmu;
   const float* kmax;
   const uint8_t* elig;
+  uint16_t* vt;   // V^T staging in the workspace: [b][h][d][S]
   int32_t B, H, S, T, F, w;
   int32_t gq;     // query granules per item
   int32_t nqb;    // items per (frame, batch, head)
@@ -133,6 +134,7 @@ struct sfa_plan {
   int32_t S;
   int32_t gq;       // query granules per item (block_q / 16)
   int32_t waves;    // waves per attention workgroup (4 or 8)
+  int32_t stages;   // 64-key LDS stages in flight (2..4)
   int32_t nqb;      // T / block_q
   int32_t items;
   int32_t nchunk;   // norm-kernel token chunks
@@ -143,4 +145,5 @@ struct sfa_plan {
 
 // Launchers (sfa_norms.hip / sfa_fwd.hip); return a hipError_t.
 hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream);
-hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, int waves, hipStream_t stream);
+hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, int waves, int stages,
+                          hipStream_t stream);

@@ -148,15 +148,19 @@ def test_tile_override_errors(L):
     h = ctypes.c_void_p()
     g = _geom()
     for bq in (8, 32, 96, 272, -16):     # not a multiple of 16, not dividing 48, too large
-        opt = _lib.PlanOptions(bq, 0)
+        opt = _lib.PlanOptions(bq, 0, 0)
         assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == \
             _lib.SFA_ERR_UNSUPPORTED, bq
     for waves in (1, 2, 6, 16, -4):
-        opt = _lib.PlanOptions(0, waves)
+        opt = _lib.PlanOptions(0, waves, 0)
         assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == \
             _lib.SFA_ERR_UNSUPPORTED, waves
+    for stages in (1, 5, -2):
+        opt = _lib.PlanOptions(0, 0, stages)
+        assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == \
+            _lib.SFA_ERR_UNSUPPORTED, stages
     for bq, waves in ((16, 0), (48, 4), (0, 8)):
-        opt = _lib.PlanOptions(bq, waves)
+        opt = _lib.PlanOptions(bq, waves, 3)
         assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == 0
         info = _lib.PlanInfo()
         assert L.sfa_plan_get_info(h, ctypes.byref(info)) == 0
