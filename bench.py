@@ -1,11 +1,13 @@
-"""Benchmark: one step = the whole hot path (norm array + attention kernel) over the
+"""Benchmark: one step = the whole hot path (prologue + attention kernel) over the
 720p-shaped layer (reference frame + 13 frames x 3600 tokens, 12 heads, d = 128,
 window +-2, batch 1) on one MI355X. Prints one JSON line.
 
 value  = active-block TFLOP/s of the step: 4*d flops per visible (query, key)
          pair, divided by the wall time per step (sfa_norms + sfa_fwd).
-roofline = the attention kernel alone, timed with HIP events on its stream,
-         against the bf16 dense MFMA peak.
+roofline = the attention kernel alone (sfa_fwd is exactly one launch), timed
+         with HIP events on its stream, against the bf16 dense MFMA peak;
+         traffic = its HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
+         (profiles/), null if the kernel source changed since.
 cpu_baseline = the fp64 CPU oracle on a bounded sample of the same layer.
 """
 import argparse
@@ -20,7 +22,31 @@ if ROOT not in sys.path:
 
 METRIC = "active-block attention TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (no sparsity)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_720p.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_720p_traffic.json")
+KERNEL_SOURCES = ("sparse_attention_frame_amd/csrc/sfa_fwd.hip",
+                  "sparse_attention_frame_amd/csrc/sfa_internal.h")
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention-kernel launch from the committed rocprofv3 counters,
+    or None when the kernel source changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
 
 
 def log(msg):
@@ -94,7 +120,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        sfa.norms(plan, q, k, workspace=ws, stream=stream)
+        sfa.norms(plan, q, k, v, workspace=ws, stream=stream)
         sfa.fwd(plan, q, k, v, out=out, workspace=ws, stream=stream)
 
     log("bench: warmup")
@@ -108,7 +134,7 @@ def main():
     t0 = time.perf_counter()
     for e in ev:
         e[0].record(stream)
-        sfa.norms(plan, q, k, workspace=ws, stream=stream)
+        sfa.norms(plan, q, k, v, workspace=ws, stream=stream)
         e[1].record(stream)
         sfa.fwd(plan, q, k, v, out=out, workspace=ws, stream=stream)
         e[2].record(stream)
@@ -126,10 +152,7 @@ def main():
     st = sfa.head_stats(plan, ws)
     assert torch.isfinite(out.float()).all(), "non-finite output"
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    traffic = measured_traffic()
 
     res = {
         "metric": METRIC,

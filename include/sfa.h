@@ -115,20 +115,22 @@ int sfa_plan_key_ranges(const sfa_plan* plan, int32_t query_frame, int32_t range
  * one (batch, head, frame) key stream land on one XCD. */
 int sfa_plan_item(const sfa_plan* plan, int32_t index, int32_t item[4]);
 
-/* Precompute the norm array for the fixed maximum (section "Unchaining
- * softmax"): per (b, h) the key mean mu, max_j ||k_j - mu||, max_i ||q_i||,
- * the bound and the eligibility flag; per row ||q_i|| and <q_i, mu>. Reads q
- * and k once and k a second time; fp32; writes only into `workspace`.
- * Deterministic (fixed reduction order, no atomics). */
-int sfa_norms(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, void* workspace,
+/* Memory-bound prologue of the attention, written into `workspace` only:
+ *  - the norm array of the fixed maximum (section "Unchaining softmax"): per
+ *    (b, h) the key mean mu, max_j ||k_j - mu||, max_i ||q_i||, the bound and
+ *    the eligibility flag; per row ||q_i|| and <q_i, mu> (fp32; q read once,
+ *    k twice; fixed reduction order, no atomics, so bit-deterministic);
+ *  - V^T [b][h][d][S] in bf16, the layout the attention kernel reads.
+ * Must run on the current q, k and v before sfa_fwd. */
+int sfa_norms(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, void* workspace,
               size_t workspace_bytes, void* stream);
 
-/* The attention: a memory-bound pass stages V^T [b][h][d][S] in the workspace,
- * then the attention kernel makes one pass over each query block's
+/* The attention kernel (one launch): one pass over each query block's
  * reference-frame and window key granules, with the fixed maximum for eligible
- * heads and the online softmax for the others. Requires sfa_norms to have run
- * on the same q, k and workspace earlier on the stream. o may not alias q, k
- * or v. */
+ * heads and the online softmax for the others. Reads q and k from their
+ * tensors and V^T from the workspace, so sfa_norms must have run on the same
+ * q, k, v and workspace earlier on the stream; v itself is only validated. o
+ * may not alias q, k or v. */
 int sfa_fwd(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_tensor o,
             void* workspace, size_t workspace_bytes, void* stream);
 

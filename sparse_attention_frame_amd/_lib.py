@@ -68,7 +68,7 @@ def _declare(lib):
         "sfa_plan_get_info": (ctypes.c_int, [P, ctypes.POINTER(PlanInfo)]),
         "sfa_plan_key_ranges": (ctypes.c_int, [P, ctypes.c_int32, i32p, i32p]),
         "sfa_plan_item": (ctypes.c_int, [P, ctypes.c_int32, i32p]),
-        "sfa_norms": (ctypes.c_int, [P, Tensor, Tensor, P, ctypes.c_size_t, P]),
+        "sfa_norms": (ctypes.c_int, [P, Tensor, Tensor, Tensor, P, ctypes.c_size_t, P]),
         "sfa_fwd": (ctypes.c_int, [P, Tensor, Tensor, Tensor, Tensor, P, ctypes.c_size_t, P]),
         "sfa_attention": (ctypes.c_int, [P, Tensor, Tensor, Tensor, Tensor, P, ctypes.c_size_t,
                                          P]),

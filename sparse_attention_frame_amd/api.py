@@ -104,11 +104,12 @@ def _ws(plan, workspace, device):
     return workspace
 
 
-def sfa_norms(plan: Plan, q, k, workspace=None, stream=None):
+def sfa_norms(plan: Plan, q, k, v, workspace=None, stream=None):
+    """Prologue: norm array (from q, k) and V^T staging (from v) into the workspace."""
     ws = _ws(plan, workspace, q.device)
     check(lib().sfa_norms(plan.handle, as_tensor(q, plan, "q"), as_tensor(k, plan, "k"),
-                          ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)),
-          "sfa_norms")
+                          as_tensor(v, plan, "v"), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                          _stream_ptr(stream)), "sfa_norms")
     return ws
 
 

@@ -148,13 +148,17 @@ bool ranges_overlap(const sfa_plan* p, const sfa_tensor& a, const sfa_tensor& b)
   return alo < bhi && blo < ahi;
 }
 
-NormParams norm_params(const sfa_plan* p, const sfa_tensor& q, const sfa_tensor& k, void* ws) {
+NormParams norm_params(const sfa_plan* p, const sfa_tensor& q, const sfa_tensor& k,
+                       const sfa_tensor& v, void* ws) {
   char* base = static_cast<char*>(ws);
   NormParams n;
   n.q = static_cast<const uint16_t*>(q.data);
   n.k = static_cast<const uint16_t*>(k.data);
+  n.v = static_cast<const uint16_t*>(v.data);
   n.qsb = q.stride_b; n.qss = q.stride_s; n.qsh = q.stride_h;
   n.ksb = k.stride_b; n.kss = k.stride_s; n.ksh = k.stride_h;
+  n.vsb = v.stride_b; n.vss = v.stride_s; n.vsh = v.stride_h;
+  n.vt = reinterpret_cast<uint16_t*>(base + p->ws.vt);
   n.mu = reinterpret_cast<float*>(base + p->ws.mu);
   n.kmax = reinterpret_cast<float*>(base + p->ws.kmax);
   n.qmax = reinterpret_cast<float*>(base + p->ws.qmax);
@@ -227,15 +231,16 @@ int sfa_plan_item(const sfa_plan* p, int32_t index, int32_t item[4]) {
   return SFA_OK;
 }
 
-int sfa_norms(const sfa_plan* p, sfa_tensor q, sfa_tensor k, void* ws, size_t ws_bytes,
-              void* stream) {
+int sfa_norms(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, void* ws,
+              size_t ws_bytes, void* stream) {
   if (!p || !ws) return SFA_ERR_INVALID;
   if (ws_bytes < p->ws.total) return SFA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return SFA_ERR_UNSUPPORTED;
   int st = check_tensor(q);
   if (st == SFA_OK) st = check_tensor(k);
+  if (st == SFA_OK) st = check_tensor(v);
   if (st != SFA_OK) return st;
-  const NormParams n = norm_params(p, q, k, ws);
+  const NormParams n = norm_params(p, q, k, v, ws);
   return hip_status(sfa_launch_norms(n, static_cast<hipStream_t>(stream)));
 }
 
@@ -265,7 +270,7 @@ int sfa_fwd(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_ten
   f.qmu = reinterpret_cast<const float*>(base + p->ws.qmu);
   f.kmax = reinterpret_cast<const float*>(base + p->ws.kmax);
   f.elig = reinterpret_cast<const uint8_t*>(base + p->ws.elig);
-  f.vt = reinterpret_cast<uint16_t*>(base + p->ws.vt);
+  f.vt = reinterpret_cast<const uint16_t*>(base + p->ws.vt);
   f.B = p->g.batch; f.H = p->g.heads; f.S = p->S; f.T = p->g.tokens_per_frame;
   f.F = p->g.frames; f.w = p->g.window;
   f.gq = p->gq; f.nqb = p->nqb; f.items = p->items;
@@ -277,7 +282,7 @@ int sfa_fwd(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_ten
 
 int sfa_attention(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_tensor o,
                   void* ws, size_t ws_bytes, void* stream) {
-  int st = sfa_norms(p, q, k, ws, ws_bytes, stream);
+  int st = sfa_norms(p, q, k, v, ws, ws_bytes, stream);
   if (st != SFA_OK) return st;
   return sfa_fwd(p, q, k, v, o, ws, ws_bytes, stream);
 }

@@ -35,9 +35,9 @@
 //     16-byte LDS load per lane; the O accumulator lane again holds one query
 //     row, so the online rescale and the final 1/l are per-lane scalars.
 //
-// Staging: a memory-bound pre-pass writes V^T [b][h][d][S] into the workspace
-// (LDS transpose reads run at well under half the rate of plain 16-byte reads
-// on gfx950). K rows and V^T granules then go from HBM straight into LDS by
+// Staging: the memory-bound prologue (sfa_norms) writes V^T [b][h][d][S] into
+// the workspace (LDS transpose reads run at well under half the rate of plain
+// 16-byte reads on gfx950). K rows and V^T granules then go from HBM straight into LDS by
 // DMA (global_load_lds_dwordx4: no registers, no VALU), double-buffered per
 // 64-key stage. 16-byte chunks are XOR-swizzled through the DMA source address
 // so the operand reads are free of bank conflicts:
@@ -635,49 +635,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void fwd_kernel(FwdParams p) {
     A::run_online(p, it, lds);
 }
 
-// V^T staging: one block per (64-token chunk, b*H + h). Rows of V are read as
-// 16-byte pieces into an LDS tile [token][d] and written out as 16-byte runs
-// of 8 consecutive tokens of one dimension: vt[b][h][d][s].
-template <int D>
-__global__ __launch_bounds__(256) void vt_kernel(FwdParams p) {
-  constexpr int CHUNK = 64;
-  constexpr int PITCH = D + 8;  // elements; keeps the column reads off one bank
-  __shared__ __attribute__((aligned(16))) uint16_t tile[CHUNK * PITCH];
-  const int s0 = blockIdx.x * CHUNK;
-  const int bh = blockIdx.y;
-  const int b = bh / p.H, h = bh - b * p.H;
-  const int n = min(CHUNK, p.S - s0);
-  const uint16_t* src = p.v + b * p.vsb + h * p.vsh;
-  for (int idx = threadIdx.x; idx < CHUNK * (D / 8); idx += 256) {
-    const int tok = idx / (D / 8), c = idx % (D / 8);
-    if (tok < n)
-      *reinterpret_cast<uint4*>(&tile[tok * PITCH + 8 * c]) =
-          *reinterpret_cast<const uint4*>(src + int64_t(s0 + tok) * p.vss + 8 * c);
-  }
-  __syncthreads();
-  uint16_t* dst = p.vt + int64_t(bh) * D * p.S;
-  for (int idx = threadIdx.x; idx < D * (CHUNK / 8); idx += 256) {
-    const int d = idx / (CHUNK / 8), c = idx % (CHUNK / 8);
-    if (8 * c < n) {  // n is a multiple of 16
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = uint32_t(tile[(8 * c + 2 * j) * PITCH + d]) |
-               (uint32_t(tile[(8 * c + 2 * j + 1) * PITCH + d]) << 16);
-      *reinterpret_cast<uint4*>(dst + int64_t(d) * p.S + s0 + 8 * c) =
-          make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
-}
-
 template <int D, int WAVES, int QT, int NBUF>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   using A = Attn<D, WAVES, QT, NBUF>;
-  hipLaunchKernelGGL(vt_kernel<D>, dim3((p.S + 63) / 64, p.B * p.H), dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   auto kern = fwd_kernel<D, WAVES, QT, NBUF>;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, A::LDS_BYTES);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.items), dim3(A::kThreads), A::LDS_BYTES, stream, p);

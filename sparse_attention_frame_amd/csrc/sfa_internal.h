@@ -98,7 +98,7 @@ struct FwdParams {
   const float* qmu;
   const float* kmax;
   const uint8_t* elig;
-  uint16_t* vt;   // V^T staging in the workspace: [b][h][d][S]
+  const uint16_t* vt;  // V^T staged by the prologue: [b][h][d][S]
   int32_t B, H, S, T, F, w;
   int32_t gq;     // query granules per item
   int32_t nqb;    // items per (frame, batch, head)
@@ -110,7 +110,9 @@ struct FwdParams {
 struct NormParams {
   const uint16_t* q;
   const uint16_t* k;
-  int64_t qsb, qss, qsh, ksb, kss, ksh;
+  const uint16_t* v;
+  int64_t qsb, qss, qsh, ksb, kss, ksh, vsb, vss, vsh;
+  uint16_t* vt;   // V^T staging in the workspace: [b][h][d][S]
   float* mu;
   float* kmax;
   float* qmax;

@@ -13,6 +13,8 @@
 //   3. stats  : per chunk, max ||k - mu||^2 and max ||q||^2, and per row
 //               ||q|| and <q, mu>                               -> pkmax, pqmax, qn, qmu
 //   4. final  : kmax, qmax, bound = scale * qmax * kmax, eligible = bound <= limit
+//   5. vt     : V^T [b][h][d][S] staged for the attention kernel, whose PV
+//               operands are then single 16-byte LDS reads
 #include "sfa_internal.h"
 
 namespace {
@@ -186,6 +188,41 @@ __global__ __launch_bounds__(256) void final_kernel(NormParams p) {
   }
 }
 
+// V^T staging: one block per (64-token chunk, b*H + h). Rows of V are read as
+// 16-byte pieces into an LDS tile [token][d] and written out as 16-byte runs
+// of 8 consecutive tokens of one dimension: vt[b][h][d][s].
+template <int D>
+__global__ __launch_bounds__(256) void vt_kernel(NormParams p) {
+  constexpr int CHUNK = 64;
+  constexpr int PITCH = D + 8;  // elements; keeps the column reads off one bank
+  __shared__ __attribute__((aligned(16))) uint16_t tile[CHUNK * PITCH];
+  const int s0 = blockIdx.x * CHUNK;
+  const int bh = blockIdx.y;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int n = min(CHUNK, p.S - s0);
+  const uint16_t* src = p.v + b * p.vsb + h * p.vsh;
+  for (int idx = threadIdx.x; idx < CHUNK * (D / 8); idx += 256) {
+    const int tok = idx / (D / 8), c = idx % (D / 8);
+    if (tok < n)
+      *reinterpret_cast<uint4*>(&tile[tok * PITCH + 8 * c]) =
+          *reinterpret_cast<const uint4*>(src + int64_t(s0 + tok) * p.vss + 8 * c);
+  }
+  __syncthreads();
+  uint16_t* dst = p.vt + int64_t(bh) * D * p.S;
+  for (int idx = threadIdx.x; idx < D * (CHUNK / 8); idx += 256) {
+    const int d = idx / (CHUNK / 8), c = idx % (CHUNK / 8);
+    if (8 * c < n) {  // n is a multiple of 16
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = uint32_t(tile[(8 * c + 2 * j) * PITCH + d]) |
+               (uint32_t(tile[(8 * c + 2 * j + 1) * PITCH + d]) << 16);
+      *reinterpret_cast<uint4*>(dst + int64_t(d) * p.S + s0 + 8 * c) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream) {
@@ -203,5 +240,12 @@ hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(final_kernel, dim3(p.B * p.H), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 vgrid((p.S + 63) / 64, p.B * p.H);
+  if (p.D == 128)
+    hipLaunchKernelGGL(vt_kernel<128>, vgrid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(vt_kernel<64>, vgrid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }

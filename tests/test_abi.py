@@ -179,13 +179,19 @@ def test_call_validation_happens_before_any_launch(L):
     good = _lib.Tensor(4096, S * 2 * 64, 2 * 64, 64)
     ws = ctypes.c_void_p(1 << 20)
     need = p.info["workspace_bytes"]
-    assert L.sfa_norms(p.handle, good, good, None, need, None) == _lib.SFA_ERR_INVALID
-    assert L.sfa_norms(p.handle, good, good, ws, need - 1, None) == _lib.SFA_ERR_INVALID
-    assert L.sfa_norms(None, good, good, ws, need, None) == _lib.SFA_ERR_INVALID
+    assert L.sfa_norms(p.handle, good, good, good, None, need, None) == _lib.SFA_ERR_INVALID
+    assert L.sfa_norms(p.handle, good, good, good, ws, need - 1, None) == _lib.SFA_ERR_INVALID
+    assert L.sfa_norms(None, good, good, good, ws, need, None) == _lib.SFA_ERR_INVALID
     bad_ptr = _lib.Tensor(4096 + 8, S * 128, 128, 64)
-    assert L.sfa_norms(p.handle, bad_ptr, good, ws, need, None) == _lib.SFA_ERR_UNSUPPORTED
+    assert L.sfa_norms(p.handle, bad_ptr, good, good, ws, need, None) == _lib.SFA_ERR_UNSUPPORTED
     bad_stride = _lib.Tensor(4096, S * 128, 130, 64)
-    assert L.sfa_norms(p.handle, good, bad_stride, ws, need, None) == _lib.SFA_ERR_UNSUPPORTED
+    assert L.sfa_norms(p.handle, good, bad_stride, good, ws, need, None) == \
+        _lib.SFA_ERR_UNSUPPORTED
+    assert L.sfa_norms(p.handle, good, good, bad_stride, ws, need, None) == \
+        _lib.SFA_ERR_UNSUPPORTED
+    huge_stride = _lib.Tensor(4096, S * (1 << 25), 1 << 25, 64)
+    assert L.sfa_norms(p.handle, good, huge_stride, good, ws, need, None) == \
+        _lib.SFA_ERR_UNSUPPORTED
     null_t = _lib.Tensor(None, S * 128, 128, 64)
     assert L.sfa_fwd(p.handle, good, good, good, null_t, ws, need, None) == _lib.SFA_ERR_INVALID
     # output aliasing an input is refused
