@@ -354,14 +354,15 @@ struct Attn {
     }
   }
 
-  // 16 MFMAs, 16 LDS reads and 48 VALU ops in lock step (3 VALU per MFMA: one
-  // 32x32x16 MFMA hides about four plain VALU ops or two exponentials when two
-  // waves share the SIMD).
+  // One pipelined region: its 16 operand reads first (the other wave of the
+  // SIMD runs its MFMAs meanwhile), then 16 MFMAs with 3 VALU ops behind each
+  // (one 32x32x16 MFMA hides about four plain VALU ops or two exponentials
+  // when two waves share the SIMD).
   __device__ static inline void interleave_16() {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
     }
   }
