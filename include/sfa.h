@@ -77,6 +77,7 @@ typedef struct sfa_plan_info {
   double active_flops;      /* 4 * d * active_pairs (q.k and p.v, 2 flops per MAC) */
   int64_t io_bytes;         /* q, k, v read once and o written once: 8 * B * S * H * d */
   size_t workspace_bytes;   /* device workspace needed by sfa_norms / sfa_fwd */
+  int32_t bound_mode;       /* the plan's bound_mode (see sfa_plan_options) */
 } sfa_plan_info;
 
 /* Validates the geometry and builds the work decomposition (host only, no HIP
@@ -91,6 +92,14 @@ typedef struct sfa_plan_options {
                              or 4 (64 rows per wave, one wave per SIMD) */
   int32_t lds_stages;     /* 64-key K/V stages in LDS: 2, 3 or 4 (default 3, which
                              selects the software-pipelined loop of the 8-wave kernel) */
+  int32_t bound_mode;     /* how the fixed maximum is bounded (section "Unchaining
+                             softmax": query norm times the largest mean-centred key norm):
+                             0 (default) per (b, h): the largest key norm of the head, one
+                             eligibility flag per head;
+                             1 per (b, h, query frame): the largest key norm over the frames
+                             that query frame sees (reference frame + window, section
+                             "Deleting the mask"), one flag per query frame. Never looser
+                             than 0; the output is the same softmax either way. */
 } sfa_plan_options;
 
 /* sfa_plan_create with overrides (options may be NULL). Values outside the
@@ -118,8 +127,10 @@ int sfa_plan_item(const sfa_plan* plan, int32_t index, int32_t item[4]);
 /* Memory-bound prologue of the attention, written into `workspace` only:
  *  - the norm array of the fixed maximum (section "Unchaining softmax"): per
  *    (b, h) the key mean mu, max_j ||k_j - mu||, max_i ||q_i||, the bound and
- *    the eligibility flag; per row ||q_i|| and <q_i, mu> (fp32; q read once,
- *    k twice; fixed reduction order, no atomics, so bit-deterministic);
+ *    the eligibility flag; per (b, h, query frame) the key-norm maximum, bound
+ *    and flag the plan's bound_mode selects; per row ||q_i|| and <q_i, mu>
+ *    (fp32; q read once, k twice; fixed reduction order, no atomics, so
+ *    bit-deterministic);
  *  - V^T [b][h][d][S] in bf16, the layout the attention kernel reads.
  * Must run on the current q, k and v before sfa_fwd. */
 int sfa_norms(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, void* workspace,
@@ -140,16 +151,30 @@ int sfa_attention(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v
 
 /* Copies per-head statistics out of the workspace after sfa_norms (synchronises
  * the stream). Each output pointer is host memory of B*H entries (mu: B*H*d) or
- * NULL to skip it. */
+ * NULL to skip it. bound = scale * max_i ||q_i|| * max_j ||k_j - mu|| (per head in
+ * both bound modes); eligible = 1 when every query frame of the head takes the
+ * fixed-maximum path. */
 int sfa_read_head_stats(const sfa_plan* plan, const void* workspace, float* mu, float* kmax,
                         float* qmax, float* bound, uint8_t* eligible, void* stream);
 
 /* Copies the per-row half of the norm array after sfa_norms (synchronises the
  * stream): qnorm[b][h][s] = ||q_s|| and qmu[b][h][s] = <q_s, mu_bh>, B*H*S floats
  * each, host memory, either may be NULL. The attention kernel derives the fixed
- * row maximum from them as M = scale * (qmu + qnorm * kmax). */
+ * row maximum from them as M = scale * (qmu + qnorm * kvis[b][h][frame(s)]). */
 int sfa_read_row_norms(const sfa_plan* plan, const void* workspace, float* qnorm, float* qmu,
                        void* stream);
+
+/* Copies the per-(b, h, query frame) half of the norm array after sfa_norms
+ * (synchronises the stream); each output is host memory of B*H*(F+1) entries,
+ * index [b][h][g], or NULL to skip it:
+ *   kvis[g]     key-norm maximum the rows of query frame g use: bound_mode 0 the
+ *               head's max_j ||k_j - mu||; bound_mode 1 the maximum over the frames
+ *               g sees of max ||k_j - mu|| within the frame;
+ *   bound[g]    scale * (max ||q_i|| over the head, mode 0, or over frame g, mode 1) * kvis[g];
+ *   eligible[g] bound[g] <= bound_limit (0 for every frame when bound_limit < 0): the
+ *               work items of frame g take the fixed-maximum path. */
+int sfa_read_frame_stats(const sfa_plan* plan, const void* workspace, float* kvis, float* bound,
+                         uint8_t* eligible, void* stream);
 
 /* Human-readable text for a status code (includes the last HIP error of the
  * calling thread for SFA_ERR_HIP). */

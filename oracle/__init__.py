@@ -21,6 +21,9 @@ What it computes, in float64:
   eligibility flag for the fixed-maximum path.
 * ``row_offsets`` -- the per-row fixed maximum used by the fixed-max path
   (a diagnostic: the output does not depend on it in exact arithmetic).
+* ``frame_stats`` / ``frame_row_offsets`` -- the same bound taken per
+  (batch, head, query frame): the largest centred key norm over the frames a
+  query frame can see, and per-query-frame eligibility.
 * ``brute.attention_brute`` -- pure-Python loops over explicitly enumerated
   visible key sets (tiny inputs only).
 
@@ -35,6 +38,8 @@ frame). No function here is "parity unpinned".
 from .attention import (  # noqa: F401
     attention,
     attention_rows,
+    frame_row_offsets,
+    frame_stats,
     head_stats,
     key_frames,
     mask_matrix,

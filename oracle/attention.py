@@ -139,3 +139,64 @@ def row_offsets(q, k, scale=None):
     qn = np.sqrt((q ** 2).sum(axis=-1))                       # [B, S, H]
     qmu = np.einsum("bshd,bhd->bsh", q, st["mu"])             # [B, S, H]
     return sc * (qmu + qn * st["kmax"][:, None, :])
+
+
+def frame_stats(q, k, frames: int, tokens_per_frame: int, window: int, scale=None,
+                bound_limit: float = 40.0):
+    """Per (batch, head, query frame) tightening of ``head_stats``.
+
+    Section "Unchaining softmax" bounds every logit by the query norm times the
+    largest mean-centred key norm. A query row only ever meets the keys of the
+    frames it can see (section "Deleting the mask": reference frame plus the
+    window), so the largest centred norm over those frames already bounds all
+    of its logits. The key mean stays the mean of the whole head: it is one
+    shift shared by every row, which softmax ignores.
+
+    mu[b, h]        = mean over all S keys of k                  (as in head_stats)
+    kfmax[b, h, f]  = max over the keys of frame f of ||k_j - mu||
+    kvis[b, h, g]   = max of kfmax[b, h, f] over the frames f visible from query frame g
+    qfmax[b, h, g]  = max over the queries of frame g of ||q_i||
+    bound[b, h, g]  = scale * qfmax * kvis
+    eligible        = bound <= bound_limit   (per query frame; inclusive;
+                                              bound_limit < 0 makes every frame ineligible)
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, S, H, d = q.shape
+    T = tokens_per_frame
+    assert S == (frames + 1) * T
+    sc = _default_scale(d, scale)
+    mu = k.mean(axis=1)                                               # [B, H, d]
+    knorm = np.sqrt(((k - mu[:, None]) ** 2).sum(axis=-1))           # [B, S, H]
+    qnorm = np.sqrt((q ** 2).sum(axis=-1))                           # [B, S, H]
+    kfmax = np.empty((B, H, frames + 1))
+    qfmax = np.empty((B, H, frames + 1))
+    for f in range(frames + 1):
+        kfmax[:, :, f] = knorm[:, f * T:(f + 1) * T, :].max(axis=1)
+        qfmax[:, :, f] = qnorm[:, f * T:(f + 1) * T, :].max(axis=1)
+    kvis = np.empty_like(kfmax)
+    for g in range(frames + 1):
+        kvis[:, :, g] = kfmax[:, :, key_frames(g, frames, window)].max(axis=-1)
+    bound = sc * qfmax * kvis
+    eligible = bound <= bound_limit
+    return {"mu": mu, "kfmax": kfmax, "kvis": kvis, "qfmax": qfmax, "bound": bound,
+            "eligible": eligible}
+
+
+def frame_row_offsets(q, k, frames: int, tokens_per_frame: int, window: int, scale=None):
+    """Fixed per-row maximum with the per-frame bound:
+    M[b, i, h] = scale * (<q_i, mu> + ||q_i|| * kvis[b, h, frame(i)]).
+
+    Raw logit minus M = centred logit minus scale * ||q_i|| * kvis, which is
+    <= 0 by Cauchy-Schwarz for every key the row can see.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[-1]
+    T = tokens_per_frame
+    sc = _default_scale(d, scale)
+    st = frame_stats(q, k, frames, T, window, scale)
+    qn = np.sqrt((q ** 2).sum(axis=-1))                       # [B, S, H]
+    qmu = np.einsum("bshd,bhd->bsh", q, st["mu"])             # [B, S, H]
+    frame = np.arange(q.shape[1]) // T
+    kv = np.transpose(st["kvis"], (0, 2, 1))[:, frame, :]     # [B, S, H]
+    return sc * (qmu + qn * kv)

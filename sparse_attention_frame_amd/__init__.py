@@ -9,6 +9,7 @@ from ._lib import SfaError, lib  # noqa: F401
 from .api import (  # noqa: F401
     Plan,
     attention,
+    frame_stats,
     fwd,
     head_stats,
     norms,
@@ -16,6 +17,7 @@ from .api import (  # noqa: F401
     sfa_attention,
     sfa_fwd,
     sfa_norms,
+    sfa_read_frame_stats,
     sfa_read_head_stats,
     sfa_read_row_norms,
 )

@@ -28,21 +28,22 @@ class Tensor(ctypes.Structure):
 
 class PlanOptions(ctypes.Structure):
     _fields_ = [("block_q", ctypes.c_int32), ("waves_per_item", ctypes.c_int32),
-                ("lds_stages", ctypes.c_int32)]
+                ("lds_stages", ctypes.c_int32), ("bound_mode", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("block_q", ctypes.c_int32), ("granule", ctypes.c_int32),
                 ("waves_per_item", ctypes.c_int32), ("items", ctypes.c_int32),
                 ("active_pairs", ctypes.c_int64), ("active_flops", ctypes.c_double),
-                ("io_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+                ("io_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
+                ("bound_mode", ctypes.c_int32)]
 
 
 # every symbol include/sfa.h declares
 EXPORTS = (
     "sfa_plan_create", "sfa_plan_create_ex", "sfa_plan_destroy", "sfa_plan_get_info",
     "sfa_plan_key_ranges", "sfa_plan_item", "sfa_norms", "sfa_fwd", "sfa_attention",
-    "sfa_read_head_stats", "sfa_read_row_norms", "sfa_status_str",
+    "sfa_read_head_stats", "sfa_read_row_norms", "sfa_read_frame_stats", "sfa_status_str",
 )
 
 _lib = None
@@ -74,6 +75,7 @@ def _declare(lib):
                                          P]),
         "sfa_read_head_stats": (ctypes.c_int, [P, P, f32p, f32p, f32p, f32p, u8p, P]),
         "sfa_read_row_norms": (ctypes.c_int, [P, P, f32p, f32p, P]),
+        "sfa_read_frame_stats": (ctypes.c_int, [P, P, f32p, f32p, u8p, P]),
         "sfa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sigs.items():

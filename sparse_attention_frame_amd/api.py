@@ -30,13 +30,13 @@ class Plan:
     def __init__(self, batch: int, heads: int, head_dim: int, frames: int,
                  tokens_per_frame: int, window: int, scale: float = 0.0,
                  bound_limit: float = 40.0, block_q: int = 0, waves: int = 0,
-                 lds_stages: int = 0):
+                 lds_stages: int = 0, bound_mode: int = 0):
         self.geometry = Geometry(batch, heads, head_dim, frames, tokens_per_frame, window,
                                  scale, bound_limit)
         handle = ctypes.c_void_p()
         L = lib()
-        if block_q or waves or lds_stages:
-            opts = PlanOptions(block_q, waves, lds_stages)
+        if block_q or waves or lds_stages or bound_mode:
+            opts = PlanOptions(block_q, waves, lds_stages, bound_mode)
             st = L.sfa_plan_create_ex(ctypes.byref(self.geometry), ctypes.byref(opts),
                                       ctypes.byref(handle))
         else:
@@ -170,9 +170,25 @@ def sfa_read_row_norms(plan: Plan, workspace, stream=None):
     return qn, qmu
 
 
+def sfa_read_frame_stats(plan: Plan, workspace, stream=None):
+    """Per (batch, head, query frame): kvis, bound and eligible, arrays [B, H, F + 1]."""
+    g = plan.geometry
+    shape = (g.batch, g.heads, g.frames + 1)
+    kvis = np.empty(shape, np.float32)
+    bound = np.empty(shape, np.float32)
+    elig = np.empty(shape, np.uint8)
+    f = ctypes.POINTER(ctypes.c_float)
+    check(lib().sfa_read_frame_stats(plan.handle, ctypes.c_void_p(workspace.data_ptr()),
+                                     kvis.ctypes.data_as(f), bound.ctypes.data_as(f),
+                                     elig.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                     _stream_ptr(stream)), "sfa_read_frame_stats")
+    return {"kvis": kvis, "bound": bound, "eligible": elig.astype(bool)}
+
+
 # short aliases
 norms = sfa_norms
 fwd = sfa_fwd
 attention = sfa_attention
 head_stats = sfa_read_head_stats
 row_norms = sfa_read_row_norms
+frame_stats = sfa_read_frame_stats

@@ -67,6 +67,8 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   if (waves != 4 && waves != 8) return SFA_ERR_UNSUPPORTED;
   const int stages = (opt && opt->lds_stages) ? opt->lds_stages : 3;
   if (stages < 2 || stages > 4) return SFA_ERR_UNSUPPORTED;
+  const int bound_mode = opt ? opt->bound_mode : 0;
+  if (bound_mode != 0 && bound_mode != 1) return SFA_ERR_UNSUPPORTED;
   int gq;
   if (block_q == 0) {
     gq = auto_block_granules(tg);
@@ -87,6 +89,7 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   p->gq = gq;
   p->waves = waves;
   p->stages = stages;
+  p->bound_mode = bound_mode;
   p->nqb = tg / gq;
   p->items = B * H * (F + 1) * p->nqb;
   p->nchunk = (p->S + kNormChunk - 1) / kNormChunk;
@@ -113,11 +116,15 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   p->ws.qmax = take(bh * 4);
   p->ws.bound = take(bh * 4);
   p->ws.elig = take(bh);                       // uint8
+  p->ws.kvis = take(bh * size_t(F + 1) * 4);   // [b][h][query frame]
+  p->ws.fbound = take(bh * size_t(F + 1) * 4);
+  p->ws.felig = take(bh * size_t(F + 1));      // uint8
   p->ws.qn = take(bh * size_t(p->S) * 4);      // [b][h][s]
   p->ws.qmu = take(bh * size_t(p->S) * 4);     // [b][h][s]
   p->ws.psum = take(size_t(p->nchunk) * bh * D * 4);  // [chunk][b][h][d]
-  p->ws.pkmax = take(size_t(p->nchunk) * bh * 4);     // [chunk][b][h], squared norms
-  p->ws.pqmax = take(size_t(p->nchunk) * bh * 4);
+  const size_t ngran = size_t(p->S) / kGranule;
+  p->ws.pkmax = take(ngran * bh * 4);          // [granule][b][h], squared norms
+  p->ws.pqmax = take(ngran * bh * 4);
   p->ws.vt = take(bh * size_t(D) * size_t(p->S) * 2);  // bf16 V^T [b][h][d][S]
   p->ws.total = off;
   *out = p;
@@ -164,6 +171,9 @@ NormParams norm_params(const sfa_plan* p, const sfa_tensor& q, const sfa_tensor&
   n.qmax = reinterpret_cast<float*>(base + p->ws.qmax);
   n.bound = reinterpret_cast<float*>(base + p->ws.bound);
   n.elig = reinterpret_cast<uint8_t*>(base + p->ws.elig);
+  n.kvis = reinterpret_cast<float*>(base + p->ws.kvis);
+  n.fbound = reinterpret_cast<float*>(base + p->ws.fbound);
+  n.felig = reinterpret_cast<uint8_t*>(base + p->ws.felig);
   n.qn = reinterpret_cast<float*>(base + p->ws.qn);
   n.qmu = reinterpret_cast<float*>(base + p->ws.qmu);
   n.psum = reinterpret_cast<float*>(base + p->ws.psum);
@@ -171,6 +181,8 @@ NormParams norm_params(const sfa_plan* p, const sfa_tensor& q, const sfa_tensor&
   n.pqmax = reinterpret_cast<float*>(base + p->ws.pqmax);
   n.B = p->g.batch; n.H = p->g.heads; n.S = p->S; n.D = p->g.head_dim;
   n.nchunk = p->nchunk;
+  n.T = p->g.tokens_per_frame; n.F = p->g.frames; n.w = p->g.window;
+  n.bound_mode = p->bound_mode;
   n.scale = p->scale;
   n.bound_limit = p->g.bound_limit;
   return n;
@@ -201,6 +213,7 @@ int sfa_plan_get_info(const sfa_plan* p, sfa_plan_info* out) {
   out->active_flops = 4.0 * p->g.head_dim * double(p->active_pairs);
   out->io_bytes = int64_t(8) * p->g.batch * p->S * p->g.heads * p->g.head_dim;
   out->workspace_bytes = p->ws.total;
+  out->bound_mode = p->bound_mode;
   return SFA_OK;
 }
 
@@ -268,8 +281,8 @@ int sfa_fwd(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_ten
   f.osb = o.stride_b; f.oss = o.stride_s; f.osh = o.stride_h;
   f.qn = reinterpret_cast<const float*>(base + p->ws.qn);
   f.qmu = reinterpret_cast<const float*>(base + p->ws.qmu);
-  f.kmax = reinterpret_cast<const float*>(base + p->ws.kmax);
-  f.elig = reinterpret_cast<const uint8_t*>(base + p->ws.elig);
+  f.kvis = reinterpret_cast<const float*>(base + p->ws.kvis);
+  f.felig = reinterpret_cast<const uint8_t*>(base + p->ws.felig);
   f.vt = reinterpret_cast<const uint16_t*>(base + p->ws.vt);
   f.B = p->g.batch; f.H = p->g.heads; f.S = p->S; f.T = p->g.tokens_per_frame;
   f.F = p->g.frames; f.w = p->g.window;
@@ -301,6 +314,25 @@ int sfa_read_head_stats(const sfa_plan* p, const void* ws, float* mu, float* kma
                  {qmax, p->ws.qmax, bh * 4},
                  {bound, p->ws.bound, bh * 4},
                  {eligible, p->ws.elig, bh}};
+  for (auto& c : copies) {
+    if (!c.dst) continue;
+    hipError_t e = hipMemcpyAsync(c.dst, base + c.off, c.bytes, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(hipStreamSynchronize(s));
+}
+
+int sfa_read_frame_stats(const sfa_plan* p, const void* ws, float* kvis, float* bound,
+                         uint8_t* eligible, void* stream) {
+  if (!p || !ws) return SFA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* base = static_cast<const char*>(ws);
+  const size_t n = size_t(p->g.batch) * p->g.heads * size_t(p->g.frames + 1);
+  struct {
+    void* dst;
+    size_t off, bytes;
+  } copies[3] = {{kvis, p->ws.kvis, n * 4}, {bound, p->ws.fbound, n * 4},
+                 {eligible, p->ws.felig, n}};
   for (auto& c : copies) {
     if (!c.dst) continue;
     hipError_t e = hipMemcpyAsync(c.dst, base + c.off, c.bytes, hipMemcpyDeviceToHost, s);

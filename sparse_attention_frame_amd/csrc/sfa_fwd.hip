@@ -6,13 +6,15 @@
 //     all visible (reference frame + window) or skipped. The reference frame's
 //     granules are simply the first granules of the same single pass: no mask
 //     predicate, no padding, no second pass, no merge.
-//   * section "Unchaining softmax" (Fig. 4): for eligible heads the softmax
-//     maximum of row i is fixed in advance to M_i = scale*(<q_i,mu> + ||q_i||*kmax)
-//     (>= every logit of the head by Cauchy-Schwarz), so the key loop has no
+//   * section "Unchaining softmax" (Fig. 4): for eligible items the softmax
+//     maximum of row i is fixed in advance to M_i = scale*(<q_i,mu> + ||q_i||*kvis)
+//     where kvis bounds ||k_j - mu|| over every key the row sees (the head's
+//     largest centred key norm, or the largest over the visible frames), so
+//     M_i >= every visible logit by Cauchy-Schwarz and the key loop has no
 //     running maximum and no accumulator rescale; the row sum stays a per-lane
-//     partial and is reduced across lanes once, at the end. Heads that are not
-//     eligible run the online softmax in the same kernel (one branch, uniform
-//     over the workgroup).
+//     partial and is reduced across lanes once, at the end. Items whose bound
+//     is too loose run the online softmax in the same kernel (one branch per
+//     (batch, head, query frame), uniform over the workgroup).
 //   * section "Proving pixels unchanged": P is rounded to bf16 and PV runs on
 //     the bf16 matrix cores with fp32 accumulation.
 //
@@ -420,7 +422,7 @@ struct Attn {
     const int rows = p.gq * 16;                 // real rows of this item
     const int row0 = it.f * p.T + it.qb * rows;
     const int64_t rowstat = (int64_t(it.b) * p.H + it.h) * p.S;
-    const float kmax = p.kmax[it.b * p.H + it.h];
+    const float kmax = p.kvis[(int64_t(it.b) * p.H + it.h) * (p.F + 1) + it.f];
     // a wave whose query tiles hold no real row only helps with the DMA
     const bool active = (wave * QT + t0) * 32 < rows;
 
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void fwd_kernel(FwdParams p) {
   using A = Attn<D, WAVES, QT, NBUF>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const Item it = sfa::decode_item(blockIdx.x, p.frame_order, p.B, p.H, p.nqb, p.items);
-  if (p.elig[it.b * p.H + it.h])
+  if (p.felig[(int64_t(it.b) * p.H + it.h) * (p.F + 1) + it.f])
     A::run_fixed(p, it, lds);
   else
     A::run_online(p, it, lds);

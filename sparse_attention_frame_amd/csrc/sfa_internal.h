@@ -85,7 +85,8 @@ __host__ __device__ inline Item decode_item(int idx, const uint16_t* frame_order
 }
 
 struct Workspace {
-  size_t mu, kmax, qmax, bound, elig, qn, qmu, psum, pkmax, pqmax, vt, total;
+  size_t mu, kmax, qmax, bound, elig, kvis, fbound, felig, qn, qmu, psum, pkmax, pqmax, vt,
+      total;
 };
 
 struct FwdParams {
@@ -96,8 +97,8 @@ struct FwdParams {
   int64_t qsb, qss, qsh, ksb, kss, ksh, vsb, vss, vsh, osb, oss, osh;
   const float* qn;
   const float* qmu;
-  const float* kmax;
-  const uint8_t* elig;
+  const float* kvis;     // [b][h][F+1]: key-norm maximum the rows of each query frame use
+  const uint8_t* felig;  // [b][h][F+1]: the items of the query frame take the fixed maximum
   const uint16_t* vt;  // V^T staged by the prologue: [b][h][d][S]
   int32_t B, H, S, T, F, w;
   int32_t gq;     // query granules per item
@@ -118,12 +119,17 @@ struct NormParams {
   float* qmax;
   float* bound;
   uint8_t* elig;
+  float* kvis;    // [b][h][F+1]
+  float* fbound;  // [b][h][F+1]
+  uint8_t* felig; // [b][h][F+1]
   float* qn;
   float* qmu;
   float* psum;
-  float* pkmax;
-  float* pqmax;
+  float* pkmax;   // [granule][b][h]: max ||k - mu||^2 over the 16 tokens of a granule
+  float* pqmax;   // [granule][b][h]: max ||q||^2
   int32_t B, H, S, D, nchunk;
+  int32_t T, F, w;
+  int32_t bound_mode;
   float scale;
   float bound_limit;
 };
@@ -138,6 +144,7 @@ struct sfa_plan {
   int32_t waves;    // waves per attention workgroup (4 or 8)
   int32_t stages;   // 64-key LDS stages in flight (2..4)
   int32_t nqb;      // T / block_q
+  int32_t bound_mode;  // 0: per-head key-norm maximum; 1: per visible frame
   int32_t items;
   int32_t nchunk;   // norm-kernel token chunks
   int64_t active_pairs;

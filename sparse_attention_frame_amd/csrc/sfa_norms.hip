@@ -10,9 +10,12 @@
 // BSHD layout): thread t owns one 8-element (16-byte) column group of one head.
 //   1. ksum   : per 64-token chunk, column sums of k            -> psum
 //   2. kmean  : mu = (sum over chunks of psum) / S              -> mu
-//   3. stats  : per chunk, max ||k - mu||^2 and max ||q||^2, and per row
-//               ||q|| and <q, mu>                               -> pkmax, pqmax, qn, qmu
-//   4. final  : kmax, qmax, bound = scale * qmax * kmax, eligible = bound <= limit
+//   3. stats  : per 16-token granule, max ||k - mu||^2 and max ||q||^2, and per
+//               row ||q|| and <q, mu>                           -> pkmax, pqmax, qn, qmu
+//   4. final  : per frame the maxima of its granules; per head kmax, qmax,
+//               bound = scale * qmax * kmax; per query frame the key-norm
+//               maximum its rows use (the head's, or the largest over the
+//               frames it sees), its bound and its eligibility flag
 //   5. vt     : V^T [b][h][d][S] staged for the attention kernel, whose PV
 //               operands are then single 16-byte LDS reads
 #include "sfa_internal.h"
@@ -146,26 +149,46 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(NormParams p) {
         const int64_t row = (int64_t(b) * p.H + h) * p.S + s;
         p.qn[row] = sqrtf(qq);
         p.qmu[row] = qm;
+        if ((s & 15) == 15) {  // last token of a granule (S and s0 are multiples of 16)
+          const int64_t at = (int64_t(s >> 4) * p.B + b) * p.H + h;
+          p.pkmax[at] = kmax2;
+          p.pqmax[at] = qmax2;
+        }
       }
-    }
-    if (active && (cg % CPR) == 0) {
-      const int64_t at = (int64_t(chunk) * p.B + b) * p.H + h;
-      p.pkmax[at] = kmax2;
-      p.pqmax[at] = qmax2;
+      if ((s & 15) == 15) kmax2 = qmax2 = 0.f;
     }
   }
 }
 
-// Per (b, h): kmax, qmax (max over the chunk partials of squared norms), the
-// bound and the eligibility flag. One block per (b, h).
+// Per (b, h), one block: the squared-norm maxima of every frame (its granules
+// in order), the head maxima kmax and qmax and the head bound; then per query
+// frame g the key-norm maximum kvis[g] its rows use, its bound and its flag:
+//   bound_mode 0: kvis[g] = kmax, bound[g] = scale * qmax * kmax;
+//   bound_mode 1: kvis[g] = max over the frames g sees (reference frame and the
+//                 video frames within the window) of the frame's key maximum,
+//                 bound[g] = scale * (max ||q|| over frame g) * kvis[g].
+// The head flag is set when every query frame of the head is eligible.
 __global__ __launch_bounds__(256) void final_kernel(NormParams p) {
+  __shared__ float kf2[sfa::kMaxFrameSlots], qf2[sfa::kMaxFrameSlots];
   __shared__ float k2s[256], q2s[256];
   const int bh = blockIdx.x;
   const int64_t stride = int64_t(p.B) * p.H;
+  const int nf = p.F + 1;
+  const int gpf = p.T / 16;  // granules per frame
+  for (int f = threadIdx.x; f < nf; f += 256) {
+    float k2 = 0.f, q2 = 0.f;
+    for (int g = f * gpf; g < (f + 1) * gpf; ++g) {
+      k2 = fmaxf(k2, p.pkmax[g * stride + bh]);
+      q2 = fmaxf(q2, p.pqmax[g * stride + bh]);
+    }
+    kf2[f] = k2;
+    qf2[f] = q2;
+  }
+  __syncthreads();
   float k2 = 0.f, q2 = 0.f;
-  for (int c = threadIdx.x; c < p.nchunk; c += 256) {
-    k2 = fmaxf(k2, p.pkmax[c * stride + bh]);
-    q2 = fmaxf(q2, p.pqmax[c * stride + bh]);
+  for (int f = threadIdx.x; f < nf; f += 256) {
+    k2 = fmaxf(k2, kf2[f]);
+    q2 = fmaxf(q2, qf2[f]);
   }
   k2s[threadIdx.x] = k2;
   q2s[threadIdx.x] = q2;
@@ -177,14 +200,35 @@ __global__ __launch_bounds__(256) void final_kernel(NormParams p) {
     }
     __syncthreads();
   }
+  const float kmax = sqrtf(k2s[0]);
+  const float qmax = sqrtf(q2s[0]);
+  const float hbound = p.scale * qmax * kmax;
+  const bool limit_ok = p.bound_limit >= 0.f;
+  int all = 1;
+  for (int g = threadIdx.x; g < nf; g += 256) {
+    float kv = kmax, fb = hbound;
+    if (p.bound_mode == 1) {
+      float m2 = kf2[0];  // the reference frame is visible to every query frame
+      if (g > 0) {
+        const int lo = max(1, g - p.w), hi = min(p.F, g + p.w);
+        for (int f = lo; f <= hi; ++f) m2 = fmaxf(m2, kf2[f]);
+      }
+      kv = sqrtf(m2);
+      fb = p.scale * sqrtf(qf2[g]) * kv;
+    }
+    const uint8_t e = (limit_ok && fb <= p.bound_limit) ? 1 : 0;
+    const int64_t at = int64_t(bh) * nf + g;
+    p.kvis[at] = kv;
+    p.fbound[at] = fb;
+    p.felig[at] = e;
+    all &= e;
+  }
+  all = __syncthreads_and(all);
   if (threadIdx.x == 0) {
-    const float kmax = sqrtf(k2s[0]);
-    const float qmax = sqrtf(q2s[0]);
-    const float bound = p.scale * qmax * kmax;
     p.kmax[bh] = kmax;
     p.qmax[bh] = qmax;
-    p.bound[bh] = bound;
-    p.elig[bh] = (p.bound_limit >= 0.f && bound <= p.bound_limit) ? 1 : 0;
+    p.bound[bh] = hbound;
+    p.elig[bh] = all ? 1 : 0;
   }
 }
 

@@ -34,6 +34,7 @@ class Workload:
     batch: int = 1
     boost_heads: Tuple[int, ...] = field(default_factory=tuple)  # q and k scaled by boost
     boost: float = 6.0
+    boost_key_frames: Tuple[int, ...] = field(default_factory=tuple)  # k of these frames scaled
 
     @property
     def seq(self) -> int:
@@ -54,6 +55,10 @@ P1080 = Workload("1080p", frames=5, tokens_per_frame=8160, heads=12, head_dim=12
 STRESS = Workload("stress", frames=13, tokens_per_frame=3600, heads=16, head_dim=128,
                   window=2, sigma_c=3.0, seed=1004, boost_heads=(3, 7, 11, 15))
 STRESS_FULL = STRESS.with_window(13, "stress_w13")
+# 720p geometry whose last video frame carries keys 6x wider than the rest (all heads): the
+# per-head bound is then loose everywhere, the per-visible-frame bound only near that frame.
+OUTLIER = Workload("outlier", frames=13, tokens_per_frame=3600, heads=12, head_dim=128,
+                   window=2, sigma_c=3.0, seed=1005, boost_key_frames=(13,))
 
 ALL = {w.name: w for w in (TINY, SMALL, P720, P1080, STRESS, STRESS_FULL)}
 
@@ -73,6 +78,9 @@ def make_inputs_np(wl: Workload):
     for h in wl.boost_heads:
         q[:, :, h, :] *= np.float32(wl.boost)
         k[:, :, h, :] *= np.float32(wl.boost)
+    T = wl.tokens_per_frame
+    for f in wl.boost_key_frames:
+        k[:, f * T:(f + 1) * T, :, :] *= np.float32(wl.boost)
     out = []
     for x in (q, k, v):
         # torch's float32 -> bfloat16 cast rounds to nearest even

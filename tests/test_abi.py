@@ -159,6 +159,17 @@ def test_tile_override_errors(L):
         opt = _lib.PlanOptions(0, 0, stages)
         assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == \
             _lib.SFA_ERR_UNSUPPORTED, stages
+    for mode in (2, -1, 7):
+        opt = _lib.PlanOptions(0, 0, 0, mode)
+        assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == \
+            _lib.SFA_ERR_UNSUPPORTED, mode
+    for mode in (0, 1):
+        opt = _lib.PlanOptions(0, 0, 0, mode)
+        assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == 0
+        info = _lib.PlanInfo()
+        assert L.sfa_plan_get_info(h, ctypes.byref(info)) == 0
+        assert info.bound_mode == mode
+        L.sfa_plan_destroy(h)
     for bq, waves in ((16, 0), (48, 4), (0, 8)):
         opt = _lib.PlanOptions(bq, waves, 3)
         assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == 0

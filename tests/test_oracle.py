@@ -284,3 +284,131 @@ def test_seeded_workload_eligibility_matches_definitions():
         assert bad == expect_bad, (name, st["bound"])
         # keep far from the knife edge so the fp32 comparison on the GPU agrees
         assert np.all(np.abs(st["bound"] - 40.0) > 1.0)
+
+
+# ------------------------------------------------------- frame bound ----
+
+def _closed_form_frames(a=(1.0, 2.0, 7.0, 3.0, 5.0)):
+    """F = 4, T = 16, d = 64, w = 1, one head. Frame f holds c + a_f*e_t (local t < 8) and
+    c - a_f*e_{t-8} (t >= 8): every frame's keys average to c, so mu = c and every centred
+    key of frame f has norm a_f exactly. Queries are 2*e_0 except local row 3 of frame g,
+    which is qg*e_0."""
+    F, T, d = 4, 16, 64
+    qg = [16.0, 8.0, 48.0, 40.0, 64.0]
+    c = np.arange(1, d + 1, dtype=np.float64) / 8.0
+    S = (F + 1) * T
+    k = np.empty((1, S, 1, d))
+    q = np.zeros((1, S, 1, d))
+    for f in range(F + 1):
+        for t in range(T):
+            j = f * T + t
+            k[0, j, 0] = c
+            if t < 8:
+                k[0, j, 0, t] += a[f]
+            else:
+                k[0, j, 0, t - 8] -= a[f]
+            q[0, j, 0, 0] = 2.0
+        q[0, f * T + 3, 0, 0] = qg[f]
+    return q, k, F, T, 1
+
+
+def test_frame_bound_closed_form_and_inclusive_threshold():
+    q, k, F, T, w = _closed_form_frames()
+    st = oracle.frame_stats(q, k, F, T, w)
+    np.testing.assert_allclose(st["mu"][0, 0], np.arange(1, 65) / 8.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(st["kfmax"][0, 0], [1, 2, 7, 3, 5], rtol=0, atol=1e-13)
+    # visible frames: 0 -> {0}; 1 -> {0,1,2}; 2 -> {0,1,2,3}; 3 -> {0,2,3,4}; 4 -> {0,3,4}
+    np.testing.assert_allclose(st["kvis"][0, 0], [1, 7, 7, 7, 5], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(st["qfmax"][0, 0], [16, 8, 48, 40, 64], rtol=0, atol=0)
+    # scale 1/8: bounds 2, 7, 42, 35, 40 -- 40 is still eligible
+    np.testing.assert_allclose(st["bound"][0, 0], [2, 7, 42, 35, 40], rtol=0, atol=1e-12)
+    assert list(st["eligible"][0, 0]) == [True, True, False, True, True]
+    # the per-head bound of the same inputs is 64 * 7 / 8 = 56: the whole head would fail
+    hs = oracle.head_stats(q, k)
+    np.testing.assert_allclose(hs["bound"][0, 0], 56.0, rtol=0, atol=1e-12)
+    assert not oracle.frame_stats(q, k, F, T, w, bound_limit=-1.0)["eligible"].any()
+
+
+def test_frame_bound_counts_the_reference_frame():
+    """Reference frame widest except for frame 2: frame 4 (sees 0, 3, 4) takes its bound from
+    the reference frame's keys, frames 1..3 from frame 2's."""
+    q, k, F, T, w = _closed_form_frames(a=(6.0, 2.0, 7.0, 3.0, 5.0))
+    st = oracle.frame_stats(q, k, F, T, w)
+    np.testing.assert_allclose(st["kvis"][0, 0], [6, 7, 7, 7, 6], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(st["bound"][0, 0], [12, 7, 42, 35, 48], rtol=0, atol=1e-12)
+    assert list(st["eligible"][0, 0]) == [True, True, False, True, False]
+
+
+def test_frame_row_offset_is_tight_on_the_widest_visible_key():
+    """Row 3 of frames 1 and 4 points along e_0, the direction of the widest key they can
+    see (frame 2's key 0 with norm 7, frame 4's key 0 with norm 5): M equals the row's true
+    maximum logit there."""
+    q, k, F, T, w = _closed_form_frames()
+    M = oracle.frame_row_offsets(q, k, F, T, w)
+    mask = oracle.mask_matrix(F, T, w)
+    s = (q[0, :, 0] @ k[0, :, 0].T) / 8.0
+    smax = np.where(mask, s, -np.inf).max(axis=1)
+    assert np.all(M[0, :, 0] - smax >= -1e-12)
+    for g in (1, 4):
+        i = g * T + 3
+        np.testing.assert_allclose(M[0, i, 0], smax[i], rtol=0, atol=1e-12)
+
+
+def test_frame_bound_matches_brute_force_tiny():
+    """Visible key sets enumerated as in the brute-force module, norms with math.fsum."""
+    from oracle.brute import visible_keys
+
+    wl = W.TINY
+    q, k, _ = W.make_inputs_np(wl)
+    F, T, w, d = wl.frames, wl.tokens_per_frame, wl.window, wl.head_dim
+    st = oracle.frame_stats(q, k, F, T, w)
+    sc = 1.0 / math.sqrt(d)
+    for h in range(wl.heads):
+        mu = [math.fsum(float(k[0, j, h, t]) for j in range(wl.seq)) / wl.seq for t in range(d)]
+        for g in range(F + 1):
+            keys = visible_keys(g * T, F, T, w)
+            kv = max(math.sqrt(math.fsum((float(k[0, j, h, t]) - mu[t]) ** 2 for t in range(d)))
+                     for j in keys)
+            qf = max(math.sqrt(math.fsum(float(q[0, i, h, t]) ** 2 for t in range(d)))
+                     for i in range(g * T, (g + 1) * T))
+            assert abs(st["kvis"][0, h, g] - kv) <= 1e-12
+            assert abs(st["qfmax"][0, h, g] - qf) <= 1e-12
+            assert abs(st["bound"][0, h, g] - sc * qf * kv) <= 1e-12
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_frame_bound_is_tighter_and_still_bounds_every_visible_logit(name):
+    wl = W.ALL[name]
+    q, k, _ = W.make_inputs_np(wl)
+    F, T, w = wl.frames, wl.tokens_per_frame, wl.window
+    fs = oracle.frame_stats(q, k, F, T, w)
+    hs = oracle.head_stats(q, k)
+    # a max over a subset, and every frame is visible from some query frame
+    assert np.all(fs["kvis"] <= hs["kmax"][..., None])
+    np.testing.assert_array_equal(fs["kvis"].max(axis=-1), hs["kmax"])
+    np.testing.assert_array_equal(fs["kfmax"].max(axis=-1), hs["kmax"])
+    np.testing.assert_array_equal(fs["qfmax"].max(axis=-1), hs["qmax"])
+    assert np.all(fs["bound"] <= hs["bound"][..., None] + 1e-12)
+    Mf = oracle.frame_row_offsets(q, k, F, T, w)
+    Mh = oracle.row_offsets(q, k)
+    assert np.all(Mf <= Mh + 1e-9)
+    mask = oracle.mask_matrix(F, T, w)
+    sc = 1.0 / math.sqrt(wl.head_dim)
+    frame = np.arange(wl.seq) // T
+    for h in range(wl.heads):
+        s = sc * (q[0, :, h].astype(np.float64) @ k[0, :, h].astype(np.float64).T)
+        smax = np.where(mask, s, -np.inf).max(axis=1)
+        smin = np.where(mask, s, np.inf).min(axis=1)
+        assert (Mf[0, :, h] - smax).min() >= -1e-9
+        assert np.all(Mf[0, :, h] - smin <= 2 * fs["bound"][0, h, frame] + 1e-9)
+
+
+def test_frame_bound_full_window_reduces_to_head_bound():
+    """w >= F: every video frame sees every frame, so its kvis is the head's kmax."""
+    wl = W.TINY
+    q, k, _ = W.make_inputs_np(wl)
+    fs = oracle.frame_stats(q, k, wl.frames, wl.tokens_per_frame, wl.frames)
+    hs = oracle.head_stats(q, k)
+    np.testing.assert_array_equal(fs["kvis"][:, :, 1:],
+                                  np.broadcast_to(hs["kmax"][..., None], fs["kvis"][:, :, 1:].shape))
+    np.testing.assert_array_equal(fs["kvis"][:, :, 0], fs["kfmax"][:, :, 0])
