@@ -94,6 +94,12 @@ def main():
     ap.add_argument("--waves", type=int, default=0, help="override waves per workgroup (4 or 8)")
     ap.add_argument("--block-q", type=int, default=0, help="override query rows per work item")
     ap.add_argument("--lds-stages", type=int, default=0, help="override K/V stages in flight")
+    ap.add_argument("--bound-mode", type=int, default=0,
+                    help="0: per-head bound (default); 1: per-visible-frame bound")
+    ap.add_argument("--head-groups", type=int, default=1,
+                    help="split the heads into this many groups (sfa_attention_groups)")
+    ap.add_argument("--group-streams", type=int, default=0,
+                    help="streams the head groups are spread over (0: the current stream)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one elementwise copy of this size (calibrates HBM counters)")
     args = ap.parse_args()
@@ -108,18 +114,32 @@ def main():
     import sparse_attention_frame_amd as sfa
     from sparse_attention_frame_amd import workloads as W
 
-    wl = W.ALL[args.workload]
+    wl = {**W.ALL, W.OUTLIER.name: W.OUTLIER}[args.workload]
     log(f"bench: generating {wl.name} inputs")
     q_np, k_np, v_np = W.make_inputs_np(wl)
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q_np, k_np, v_np))
     plan = sfa.Plan.for_workload(wl, waves=args.waves, block_q=args.block_q,
-                                 lds_stages=args.lds_stages)
+                                 lds_stages=args.lds_stages, bound_mode=args.bound_mode)
     ws = plan.workspace(dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
+    G = args.head_groups
+    if G < 1 or wl.heads % G:
+        print(f"--head-groups must divide the {wl.heads} heads", file=sys.stderr)
+        sys.exit(2)
+    if G > 1:
+        gplan = sfa.Plan(wl.batch, wl.heads // G, wl.head_dim, wl.frames, wl.tokens_per_frame,
+                         wl.window, waves=args.waves, block_q=args.block_q,
+                         lds_stages=args.lds_stages, bound_mode=args.bound_mode)
+        gws = torch.empty(G * gplan.info["workspace_bytes"], dtype=torch.uint8, device=dev)
+        gstreams = [torch.cuda.Stream() for _ in range(args.group_streams)]
 
     def step():
+        if G > 1:
+            sfa.attention_groups(gplan, G, q, k, v, out=out, workspace=gws, streams=gstreams,
+                                 stream=stream)
+            return
         sfa.norms(plan, q, k, v, workspace=ws, stream=stream)
         sfa.fwd(plan, q, k, v, out=out, workspace=ws, stream=stream)
 
@@ -134,9 +154,13 @@ def main():
     t0 = time.perf_counter()
     for e in ev:
         e[0].record(stream)
-        sfa.norms(plan, q, k, v, workspace=ws, stream=stream)
-        e[1].record(stream)
-        sfa.fwd(plan, q, k, v, out=out, workspace=ws, stream=stream)
+        if G > 1:           # one call: the split between prologue and kernel is not timed
+            e[1].record(stream)
+            step()
+        else:
+            sfa.norms(plan, q, k, v, workspace=ws, stream=stream)
+            e[1].record(stream)
+            sfa.fwd(plan, q, k, v, out=out, workspace=ws, stream=stream)
         e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -148,8 +172,11 @@ def main():
     info = plan.info
     flops = info["active_flops"]
     value = flops / (ms_step * 1e-3) / 1e12
-    fwd_tf = flops / (fwd_ms * 1e-3) / 1e12
+    fwd_tf = flops / (fwd_ms * 1e-3) / 1e12   # with head groups: the whole grouped call
+    if G > 1:
+        sfa.norms(plan, q, k, v, workspace=ws, stream=stream)   # for the flag count below
     st = sfa.head_stats(plan, ws)
+    fst = sfa.frame_stats(plan, ws)
     assert torch.isfinite(out.float()).all(), "non-finite output"
 
     traffic = measured_traffic()
@@ -173,15 +200,20 @@ def main():
                    "block_q": info["block_q"], "waves": info["waves_per_item"],
                    "items": info["items"],
                    "active_gflop": round(flops / 1e9, 1),
-                   "eligible_heads": int(st["eligible"].sum()), "heads": wl.heads},
+                   "eligible_heads": int(st["eligible"].sum()), "heads": wl.heads,
+                   "bound_mode": args.bound_mode,
+                   "eligible_query_frames": int(fst["eligible"].sum()),
+                   "query_frames": int(fst["eligible"].size),
+                   "head_groups": G, "group_streams": args.group_streams},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_ms, 4),
         "fwd_min_ms": round(fwd_min, 4),
         "norms_ms": round(norms_ms, 4),
-        "roofline": {"bound": "mfma", "kernel": "fwd_kernel",
+        "roofline": {"bound": "mfma",
+                     "kernel": "fwd_kernel" if G == 1 else f"whole step ({G} head groups)",
                      "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic if G == 1 and args.bound_mode == 0 else None},
     }
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 2

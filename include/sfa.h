@@ -149,6 +149,22 @@ int sfa_fwd(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_
 int sfa_attention(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v,
                   sfa_tensor o, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Head-group split (section "Hiding collectives": heads are independent and the
+ * mask does not depend on them, so they can be processed in groups, each group
+ * a pipeline step of its own). Runs sfa_attention on `groups` consecutive head
+ * groups of q, k, v, o, each of `group_plan`'s geometry (its `heads` is the group
+ * size; the tensors hold groups * heads heads, group g being heads
+ * [g*heads, (g+1)*heads)). Group g uses workspace bytes [g*W, (g+1)*W) with W =
+ * the group plan's workspace_bytes (so workspace_bytes >= groups * W) and is
+ * launched on group_streams[g % nstreams] (or on `stream` when nstreams is 0).
+ * The group streams first wait for the work already queued on `stream`, and
+ * `stream` then waits for every group, so callers order against `stream` only.
+ * Results are bitwise identical to one sfa_attention over all heads. The events
+ * that order the streams are created and released inside the call. */
+int sfa_attention_groups(const sfa_plan* group_plan, int32_t groups, sfa_tensor q, sfa_tensor k,
+                         sfa_tensor v, sfa_tensor o, void* workspace, size_t workspace_bytes,
+                         void* stream, void* const* group_streams, int32_t nstreams);
+
 /* Copies per-head statistics out of the workspace after sfa_norms (synchronises
  * the stream). Each output pointer is host memory of B*H entries (mu: B*H*d) or
  * NULL to skip it. bound = scale * max_i ||q_i|| * max_j ||k_j - mu|| (per head in

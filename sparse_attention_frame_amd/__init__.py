@@ -9,12 +9,14 @@ from ._lib import SfaError, lib  # noqa: F401
 from .api import (  # noqa: F401
     Plan,
     attention,
+    attention_groups,
     frame_stats,
     fwd,
     head_stats,
     norms,
     row_norms,
     sfa_attention,
+    sfa_attention_groups,
     sfa_fwd,
     sfa_norms,
     sfa_read_frame_stats,

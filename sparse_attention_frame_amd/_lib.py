@@ -43,7 +43,8 @@ class PlanInfo(ctypes.Structure):
 EXPORTS = (
     "sfa_plan_create", "sfa_plan_create_ex", "sfa_plan_destroy", "sfa_plan_get_info",
     "sfa_plan_key_ranges", "sfa_plan_item", "sfa_norms", "sfa_fwd", "sfa_attention",
-    "sfa_read_head_stats", "sfa_read_row_norms", "sfa_read_frame_stats", "sfa_status_str",
+    "sfa_attention_groups", "sfa_read_head_stats", "sfa_read_row_norms", "sfa_read_frame_stats",
+    "sfa_status_str",
 )
 
 _lib = None
@@ -73,6 +74,9 @@ def _declare(lib):
         "sfa_fwd": (ctypes.c_int, [P, Tensor, Tensor, Tensor, Tensor, P, ctypes.c_size_t, P]),
         "sfa_attention": (ctypes.c_int, [P, Tensor, Tensor, Tensor, Tensor, P, ctypes.c_size_t,
                                          P]),
+        "sfa_attention_groups": (ctypes.c_int, [P, ctypes.c_int32, Tensor, Tensor, Tensor, Tensor,
+                                                P, ctypes.c_size_t, P, ctypes.POINTER(P),
+                                                ctypes.c_int32]),
         "sfa_read_head_stats": (ctypes.c_int, [P, P, f32p, f32p, f32p, f32p, u8p, P]),
         "sfa_read_row_norms": (ctypes.c_int, [P, P, f32p, f32p, P]),
         "sfa_read_frame_stats": (ctypes.c_int, [P, P, f32p, f32p, u8p, P]),

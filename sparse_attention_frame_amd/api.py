@@ -141,6 +141,33 @@ def sfa_attention(plan: Plan, q, k, v, out=None, workspace=None, stream=None):
     return out, ws
 
 
+def sfa_attention_groups(group_plan: Plan, groups: int, q, k, v, out=None, workspace=None,
+                         streams=(), stream=None):
+    """sfa_attention on `groups` consecutive head groups of q, k, v ([B, S, groups*Hg, d]),
+    group g on streams[g % len(streams)] (or on `stream` when streams is empty), each with
+    its own slice of the workspace. Returns (out, workspace)."""
+    import torch
+
+    g = group_plan.geometry
+    shape = (g.batch, group_plan.seq, groups * g.heads, g.head_dim)
+    for name, t in (("q", q), ("k", k), ("v", v)) + ((("o", out),) if out is not None else ()):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or tuple(t.shape) != shape or \
+                t.stride(3) != 1:
+            raise ValueError(f"{name} must be a bf16 device tensor {shape} with contiguous d")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if workspace is None:
+        workspace = torch.empty(groups * group_plan.info["workspace_bytes"], dtype=torch.uint8,
+                                device=q.device)
+    ts = [Tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2)) for t in (q, k, v, out)]
+    arr = (ctypes.c_void_p * max(1, len(streams)))(*[s.cuda_stream for s in streams])
+    check(lib().sfa_attention_groups(group_plan.handle, groups, *ts,
+                                     ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                     _stream_ptr(stream), arr, len(streams)),
+          "sfa_attention_groups")
+    return out, workspace
+
+
 def sfa_read_head_stats(plan: Plan, workspace, stream=None):
     g = plan.geometry
     bh = g.batch * g.heads
@@ -189,6 +216,7 @@ def sfa_read_frame_stats(plan: Plan, workspace, stream=None):
 norms = sfa_norms
 fwd = sfa_fwd
 attention = sfa_attention
+attention_groups = sfa_attention_groups
 head_stats = sfa_read_head_stats
 row_norms = sfa_read_row_norms
 frame_stats = sfa_read_frame_stats

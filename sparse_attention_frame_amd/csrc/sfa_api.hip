@@ -300,6 +300,59 @@ int sfa_attention(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, s
   return sfa_fwd(p, q, k, v, o, ws, ws_bytes, stream);
 }
 
+int sfa_attention_groups(const sfa_plan* p, int32_t groups, sfa_tensor q, sfa_tensor k,
+                         sfa_tensor v, sfa_tensor o, void* ws, size_t ws_bytes, void* stream,
+                         void* const* group_streams, int32_t nstreams) {
+  if (!p || !ws || groups < 1 || nstreams < 0) return SFA_ERR_INVALID;
+  if (nstreams > 0 && !group_streams) return SFA_ERR_INVALID;
+  const size_t per = p->ws.total;
+  if (ws_bytes / size_t(groups) < per) return SFA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return SFA_ERR_UNSUPPORTED;
+  // per-group views: the same strides, data advanced by whole head groups
+  auto view = [&](const sfa_tensor& t, int g) {
+    sfa_tensor r = t;
+    r.data = static_cast<char*>(t.data) + int64_t(g) * p->g.heads * t.stride_h * 2;
+    return r;
+  };
+  hipStream_t main = static_cast<hipStream_t>(stream);
+  const int ns = nstreams < groups ? nstreams : groups;  // streams actually used
+  hipEvent_t fork = nullptr;
+  hipEvent_t joins[64];
+  if (ns > 64) return SFA_ERR_UNSUPPORTED;
+  int st = SFA_OK;
+  if (ns > 0) {
+    hipError_t e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(fork, main);
+    for (int i = 0; e == hipSuccess && i < ns; ++i)
+      e = hipStreamWaitEvent(static_cast<hipStream_t>(group_streams[i]), fork, 0);
+    if (e != hipSuccess) {
+      if (fork) hipEventDestroy(fork);
+      return hip_status(e);
+    }
+  }
+  for (int g = 0; g < groups && st == SFA_OK; ++g) {
+    void* s = ns > 0 ? group_streams[g % ns] : stream;
+    st = sfa_attention(p, view(q, g), view(k, g), view(v, g), view(o, g),
+                       static_cast<char*>(ws) + size_t(g) * per, per, s);
+  }
+  if (ns > 0) {
+    // join: the caller's stream waits for every group stream (also after an
+    // error, so no group work is left unordered)
+    int made = 0;
+    hipError_t e = hipSuccess;
+    for (; made < ns && e == hipSuccess; ++made) {
+      e = hipEventCreateWithFlags(&joins[made], hipEventDisableTiming);
+      if (e != hipSuccess) break;
+      e = hipEventRecord(joins[made], static_cast<hipStream_t>(group_streams[made]));
+      if (e == hipSuccess) e = hipStreamWaitEvent(main, joins[made], 0);
+    }
+    for (int i = 0; i < made; ++i) hipEventDestroy(joins[i]);
+    hipEventDestroy(fork);
+    if (st == SFA_OK && e != hipSuccess) st = hip_status(e);
+  }
+  return st;
+}
+
 int sfa_read_head_stats(const sfa_plan* p, const void* ws, float* mu, float* kmax, float* qmax,
                         float* bound, uint8_t* eligible, void* stream) {
   if (!p || !ws) return SFA_ERR_INVALID;

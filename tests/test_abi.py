@@ -210,3 +210,23 @@ def test_call_validation_happens_before_any_launch(L):
     mis_ws = ctypes.c_void_p((1 << 20) + 16)
     assert L.sfa_fwd(p.handle, good, good, good, _lib.Tensor(1 << 30, S * 128, 128, 64), mis_ws,
                      need, None) == _lib.SFA_ERR_UNSUPPORTED
+
+
+def test_head_group_call_validation_happens_before_any_launch(L):
+    """sfa_attention_groups rejects bad arguments without touching the GPU (this runs on CPU)."""
+    p = Plan(1, 2, 64, 4, 48, 1)
+    S = p.seq
+    t = _lib.Tensor(4096, S * 4 * 64, 4 * 64, 64)         # 2 groups of 2 heads
+    per = p.info["workspace_bytes"]
+    ws = ctypes.c_void_p(1 << 20)
+    streams = (ctypes.c_void_p * 2)(None, None)
+    G = L.sfa_attention_groups
+    assert G(p.handle, 0, t, t, t, t, ws, 2 * per, None, streams, 2) == _lib.SFA_ERR_INVALID
+    assert G(p.handle, 2, t, t, t, t, ws, 2 * per - 1, None, streams, 2) == _lib.SFA_ERR_INVALID
+    assert G(p.handle, 2, t, t, t, t, None, 2 * per, None, streams, 2) == _lib.SFA_ERR_INVALID
+    assert G(p.handle, 2, t, t, t, t, ws, 2 * per, None, None, 2) == _lib.SFA_ERR_INVALID
+    assert G(p.handle, 2, t, t, t, t, ws, 2 * per, None, streams, -1) == _lib.SFA_ERR_INVALID
+    assert G(None, 2, t, t, t, t, ws, 2 * per, None, streams, 2) == _lib.SFA_ERR_INVALID
+    mis = ctypes.c_void_p((1 << 20) + 16)
+    assert G(p.handle, 2, t, t, t, t, mis, 2 * per, None, streams, 2) == \
+        _lib.SFA_ERR_UNSUPPORTED

@@ -251,3 +251,22 @@ def test_error_paths_on_device(sfa):
     assert e.value.status == -1
     with pytest.raises(ValueError):
         sfa.attention(plan, q[:, :-16], k, v)
+
+
+@pytest.mark.parametrize("name,groups,nstreams", [("small", 1, 0), ("small", 2, 2),
+                                                  ("small", 4, 3), ("small", 8, 4),
+                                                  ("720p", 3, 3)])
+def test_head_groups_are_bitwise_equal(sfa, name, groups, nstreams):
+    """Head groups on their own streams (section "Hiding collectives": heads are
+    independent) give exactly the single-launch result."""
+    wl = W.ALL[name]
+    say(f"[head_groups] {name} groups={groups} streams={nstreams}")
+    q, k, v = to_dev(*W.make_inputs_np(wl))
+    _, full, _ = run(sfa, geom(wl), q, k, v)
+    gp = sfa.Plan(wl.batch, wl.heads // groups, wl.head_dim, wl.frames, wl.tokens_per_frame,
+                  wl.window)
+    streams = [torch.cuda.Stream() for _ in range(nstreams)]
+    for rep in range(2):
+        out, _ = sfa.attention_groups(gp, groups, q, k, v, streams=streams)
+        torch.cuda.synchronize()
+        assert torch.equal(out, full), rep
