@@ -123,7 +123,7 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   p->ws.qmu = take(bh * size_t(p->S) * 4);     // [b][h][s]
   p->ws.psum = take(size_t(p->nchunk) * bh * D * 4);  // [chunk][b][h][d]
   const size_t ngran = size_t(p->S) / kGranule;
-  p->ws.pkmax = take(ngran * bh * 4);          // [granule][b][h], squared norms
+  p->ws.pkmax = take(ngran * bh * 4);          // [b][h][granule], squared norms
   p->ws.pqmax = take(ngran * bh * 4);
   p->ws.vt = take(bh * size_t(D) * size_t(p->S) * 2);  // bf16 V^T [b][h][d][S]
   p->ws.total = off;

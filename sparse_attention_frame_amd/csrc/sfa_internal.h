@@ -125,8 +125,8 @@ struct NormParams {
   float* qn;
   float* qmu;
   float* psum;
-  float* pkmax;   // [granule][b][h]: max ||k - mu||^2 over the 16 tokens of a granule
-  float* pqmax;   // [granule][b][h]: max ||q||^2
+  float* pkmax;   // [b][h][granule]: max ||k - mu||^2 over the 16 tokens of a granule
+  float* pqmax;   // [b][h][granule]: max ||q||^2
   int32_t B, H, S, D, nchunk;
   int32_t T, F, w;
   int32_t bound_mode;

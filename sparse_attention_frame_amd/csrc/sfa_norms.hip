@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(NormParams p) {
         p.qn[row] = sqrtf(qq);
         p.qmu[row] = qm;
         if ((s & 15) == 15) {  // last token of a granule (S and s0 are multiples of 16)
-          const int64_t at = (int64_t(s >> 4) * p.B + b) * p.H + h;
+          const int64_t at = (int64_t(b) * p.H + h) * (p.S >> 4) + (s >> 4);
           p.pkmax[at] = kmax2;
           p.pqmax[at] = qmax2;
         }
@@ -169,26 +169,30 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(NormParams p) {
 //                 bound[g] = scale * (max ||q|| over frame g) * kvis[g].
 // The head flag is set when every query frame of the head is eligible.
 __global__ __launch_bounds__(256) void final_kernel(NormParams p) {
-  __shared__ float kf2[sfa::kMaxFrameSlots], qf2[sfa::kMaxFrameSlots];
+  // squared norms are >= 0, so their float bit patterns order like the values
+  // and an integer max is exact (and independent of the order of updates)
+  __shared__ int kf2i[sfa::kMaxFrameSlots], qf2i[sfa::kMaxFrameSlots];
   __shared__ float k2s[256], q2s[256];
   const int bh = blockIdx.x;
-  const int64_t stride = int64_t(p.B) * p.H;
   const int nf = p.F + 1;
   const int gpf = p.T / 16;  // granules per frame
-  for (int f = threadIdx.x; f < nf; f += 256) {
-    float k2 = 0.f, q2 = 0.f;
-    for (int g = f * gpf; g < (f + 1) * gpf; ++g) {
-      k2 = fmaxf(k2, p.pkmax[g * stride + bh]);
-      q2 = fmaxf(q2, p.pqmax[g * stride + bh]);
-    }
-    kf2[f] = k2;
-    qf2[f] = q2;
+  const int ngran = p.S / 16;
+  for (int f = threadIdx.x; f < nf; f += 256) kf2i[f] = qf2i[f] = 0;
+  __syncthreads();
+  const float* pk = p.pkmax + int64_t(bh) * ngran;
+  const float* pq = p.pqmax + int64_t(bh) * ngran;
+  for (int g = threadIdx.x; g < ngran; g += 256) {
+    const int f = g / gpf;
+    atomicMax(&kf2i[f], __float_as_int(pk[g]));
+    atomicMax(&qf2i[f], __float_as_int(pq[g]));
   }
   __syncthreads();
+  auto kf2 = [&](int f) { return __int_as_float(kf2i[f]); };
+  auto qf2 = [&](int f) { return __int_as_float(qf2i[f]); };
   float k2 = 0.f, q2 = 0.f;
   for (int f = threadIdx.x; f < nf; f += 256) {
-    k2 = fmaxf(k2, kf2[f]);
-    q2 = fmaxf(q2, qf2[f]);
+    k2 = fmaxf(k2, kf2(f));
+    q2 = fmaxf(q2, qf2(f));
   }
   k2s[threadIdx.x] = k2;
   q2s[threadIdx.x] = q2;
@@ -208,13 +212,13 @@ __global__ __launch_bounds__(256) void final_kernel(NormParams p) {
   for (int g = threadIdx.x; g < nf; g += 256) {
     float kv = kmax, fb = hbound;
     if (p.bound_mode == 1) {
-      float m2 = kf2[0];  // the reference frame is visible to every query frame
+      float m2 = kf2(0);  // the reference frame is visible to every query frame
       if (g > 0) {
         const int lo = max(1, g - p.w), hi = min(p.F, g + p.w);
-        for (int f = lo; f <= hi; ++f) m2 = fmaxf(m2, kf2[f]);
+        for (int f = lo; f <= hi; ++f) m2 = fmaxf(m2, kf2(f));
       }
       kv = sqrtf(m2);
-      fb = p.scale * sqrtf(qf2[g]) * kv;
+      fb = p.scale * sqrtf(qf2(g)) * kv;
     }
     const uint8_t e = (limit_ok && fb <= p.bound_limit) ? 1 : 0;
     const int64_t at = int64_t(bh) * nf + g;
