@@ -23,7 +23,8 @@ if ROOT not in sys.path:
 METRIC = "active-block attention TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (no sparsity)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_720p_traffic.json")
-KERNEL_SOURCES = ("sparse_attention_frame_amd/csrc/sfa_fwd.hip",
+KERNEL_SOURCES = ("sparse_attention_frame_amd/csrc/sfa_attn.h",
+                  "sparse_attention_frame_amd/csrc/sfa_fwd.hip",
                   "sparse_attention_frame_amd/csrc/sfa_internal.h")
 
 
@@ -100,6 +101,8 @@ def main():
                     help="split the heads into this many groups (sfa_attention_groups)")
     ap.add_argument("--group-streams", type=int, default=0,
                     help="streams the head groups are spread over (0: the current stream)")
+    ap.add_argument("--ablation", choices=["none", "generic"], default="none",
+                    help="generic: time the generic block-sparse two-pass ablation instead")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one elementwise copy of this size (calibrates HBM counters)")
     args = ap.parse_args()
@@ -135,7 +138,14 @@ def main():
         gws = torch.empty(G * gplan.info["workspace_bytes"], dtype=torch.uint8, device=dev)
         gstreams = [torch.cuda.Stream() for _ in range(args.group_streams)]
 
+    if args.ablation == "generic":
+        gen = sfa.GenericPlan.for_workload(wl)
+        gen_ws = gen.workspace(dev)
+
     def step():
+        if args.ablation == "generic":
+            sfa.generic_attention(gen, q, k, v, out=out, workspace=gen_ws, stream=stream)
+            return
         if G > 1:
             sfa.attention_groups(gplan, G, q, k, v, out=out, workspace=gws, streams=gstreams,
                                  stream=stream)
@@ -154,7 +164,7 @@ def main():
     t0 = time.perf_counter()
     for e in ev:
         e[0].record(stream)
-        if G > 1:           # one call: the split between prologue and kernel is not timed
+        if G > 1 or args.ablation != "none":   # one call: no prologue/kernel split
             e[1].record(stream)
             step()
         else:
@@ -173,7 +183,7 @@ def main():
     flops = info["active_flops"]
     value = flops / (ms_step * 1e-3) / 1e12
     fwd_tf = flops / (fwd_ms * 1e-3) / 1e12   # with head groups: the whole grouped call
-    if G > 1:
+    if G > 1 or args.ablation != "none":
         sfa.norms(plan, q, k, v, workspace=ws, stream=stream)   # for the flag count below
     st = sfa.head_stats(plan, ws)
     fst = sfa.frame_stats(plan, ws)
@@ -204,16 +214,19 @@ def main():
                    "bound_mode": args.bound_mode,
                    "eligible_query_frames": int(fst["eligible"].sum()),
                    "query_frames": int(fst["eligible"].size),
-                   "head_groups": G, "group_streams": args.group_streams},
+                   "head_groups": G, "group_streams": args.group_streams,
+                   "ablation": args.ablation},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_ms, 4),
         "fwd_min_ms": round(fwd_min, 4),
         "norms_ms": round(norms_ms, 4),
         "roofline": {"bound": "mfma",
-                     "kernel": "fwd_kernel" if G == 1 else f"whole step ({G} head groups)",
+                     "kernel": ("whole step (generic two-pass ablation)" if args.ablation != "none"
+                                else "fwd_kernel" if G == 1 else f"whole step ({G} head groups)"),
                      "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic if G == 1 and args.bound_mode == 0 else None},
+                     "traffic": (traffic if G == 1 and args.bound_mode == 0
+                                 and args.ablation == "none" else None)},
     }
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 2

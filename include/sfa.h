@@ -192,6 +192,44 @@ int sfa_read_row_norms(const sfa_plan* plan, const void* workspace, float* qnorm
 int sfa_read_frame_stats(const sfa_plan* plan, const void* workspace, float* kvis, float* bound,
                          uint8_t* eligible, void* stream);
 
+/* ---- Ablation: generic block-sparse attention (measured, not the product path) ----
+ * The design the pages started from (section "Deleting the mask": splash-style
+ * block-sparse attention with generic tile sizes that ignore frame
+ * boundaries): query blocks of 256 rows and key blocks of 128 keys over the
+ * padded sequence, each (query block, key block) classified as empty, full or
+ * partial from the frame mask, partial blocks masked element by element, the
+ * window keys and the reference-frame keys processed as two separate
+ * online-softmax passes whose normalised outputs are merged through their
+ * log-sum-exp. Computes the same attention as sfa_attention (online softmax
+ * everywhere, no norm array); it exists to measure what the frame-aligned
+ * single-pass design saves on this hardware. */
+typedef struct sfa_generic sfa_generic;
+
+typedef struct sfa_generic_info {
+  int32_t block_q;          /* 256 */
+  int32_t block_k;          /* 128 */
+  int32_t query_blocks;     /* per (b, h): ceil(S / block_q) */
+  int32_t key_blocks;       /* per (b, h): ceil(S / block_k) */
+  int64_t full_blocks;      /* per (b, h), both passes */
+  int64_t partial_blocks;   /* per (b, h), both passes */
+  int64_t computed_pairs;   /* (query rows incl. padding) x (keys of visited blocks), all (b, h) */
+  size_t workspace_bytes;   /* device workspace of sfa_generic_attention */
+} sfa_generic_info;
+
+/* Host only; the block lists are built here. *out is NULL on error. */
+int sfa_generic_create(const sfa_geometry* geom, sfa_generic** out);
+void sfa_generic_destroy(sfa_generic* g);
+int sfa_generic_get_info(const sfa_generic* g, sfa_generic_info* out);
+/* Block class of (pass, query block, key block): 0 empty, 1 full, 2 partial;
+ * pass 0 = window keys, pass 1 = reference-frame keys. */
+int sfa_generic_block_class(const sfa_generic* g, int32_t pass, int32_t query_block,
+                            int32_t key_block, int32_t* cls);
+/* V^T staging, both passes (one launch) and the merge, on `stream`; all
+ * scratch (V^T, block lists, per-pass outputs and log-sum-exps) lives in
+ * `workspace`. Same tensor rules as sfa_fwd. */
+int sfa_generic_attention(const sfa_generic* g, sfa_tensor q, sfa_tensor k, sfa_tensor v,
+                          sfa_tensor o, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable text for a status code (includes the last HIP error of the
  * calling thread for SFA_ERR_HIP). */
 const char* sfa_status_str(int status);

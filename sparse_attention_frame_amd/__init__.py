@@ -7,17 +7,20 @@ raises if the library was not built.
 """
 from ._lib import SfaError, lib  # noqa: F401
 from .api import (  # noqa: F401
+    GenericPlan,
     Plan,
     attention,
     attention_groups,
     frame_stats,
     fwd,
+    generic_attention,
     head_stats,
     norms,
     row_norms,
     sfa_attention,
     sfa_attention_groups,
     sfa_fwd,
+    sfa_generic_attention,
     sfa_norms,
     sfa_read_frame_stats,
     sfa_read_head_stats,

@@ -39,12 +39,20 @@ class PlanInfo(ctypes.Structure):
                 ("bound_mode", ctypes.c_int32)]
 
 
+class GenericInfo(ctypes.Structure):
+    _fields_ = [("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("query_blocks", ctypes.c_int32), ("key_blocks", ctypes.c_int32),
+                ("full_blocks", ctypes.c_int64), ("partial_blocks", ctypes.c_int64),
+                ("computed_pairs", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+
+
 # every symbol include/sfa.h declares
 EXPORTS = (
     "sfa_plan_create", "sfa_plan_create_ex", "sfa_plan_destroy", "sfa_plan_get_info",
     "sfa_plan_key_ranges", "sfa_plan_item", "sfa_norms", "sfa_fwd", "sfa_attention",
     "sfa_attention_groups", "sfa_read_head_stats", "sfa_read_row_norms", "sfa_read_frame_stats",
-    "sfa_status_str",
+    "sfa_generic_create", "sfa_generic_destroy", "sfa_generic_get_info", "sfa_generic_block_class",
+    "sfa_generic_attention", "sfa_status_str",
 )
 
 _lib = None
@@ -80,6 +88,13 @@ def _declare(lib):
         "sfa_read_head_stats": (ctypes.c_int, [P, P, f32p, f32p, f32p, f32p, u8p, P]),
         "sfa_read_row_norms": (ctypes.c_int, [P, P, f32p, f32p, P]),
         "sfa_read_frame_stats": (ctypes.c_int, [P, P, f32p, f32p, u8p, P]),
+        "sfa_generic_create": (ctypes.c_int, [ctypes.POINTER(Geometry), ctypes.POINTER(P)]),
+        "sfa_generic_destroy": (None, [P]),
+        "sfa_generic_get_info": (ctypes.c_int, [P, ctypes.POINTER(GenericInfo)]),
+        "sfa_generic_block_class": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_int32, i32p]),
+        "sfa_generic_attention": (ctypes.c_int, [P, Tensor, Tensor, Tensor, Tensor, P,
+                                                 ctypes.c_size_t, P]),
         "sfa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sigs.items():

@@ -13,7 +13,7 @@ import ctypes
 import numpy as np
 
 from . import _lib
-from ._lib import Geometry, PlanInfo, PlanOptions, Tensor, check, lib
+from ._lib import GenericInfo, Geometry, PlanInfo, PlanOptions, Tensor, check, lib
 
 
 def _stream_ptr(stream):
@@ -212,6 +212,67 @@ def sfa_read_frame_stats(plan: Plan, workspace, stream=None):
     return {"kvis": kvis, "bound": bound, "eligible": elig.astype(bool)}
 
 
+class GenericPlan:
+    """Ablation (sfa_generic_create): generic 256 x 128 block-sparse tiles, element masks on
+    partial blocks, window and reference-frame keys as two passes plus a merge."""
+
+    def __init__(self, batch: int, heads: int, head_dim: int, frames: int,
+                 tokens_per_frame: int, window: int, scale: float = 0.0):
+        self.geometry = Geometry(batch, heads, head_dim, frames, tokens_per_frame, window,
+                                 scale, 40.0)
+        handle = ctypes.c_void_p()
+        check(lib().sfa_generic_create(ctypes.byref(self.geometry), ctypes.byref(handle)),
+              "sfa_generic_create")
+        self._h = handle
+        info = GenericInfo()
+        check(lib().sfa_generic_get_info(self._h, ctypes.byref(info)), "sfa_generic_get_info")
+        self.info = {name: getattr(info, name) for name, _ in GenericInfo._fields_}
+        self.seq = (frames + 1) * tokens_per_frame
+
+    @classmethod
+    def for_workload(cls, wl, **kw):
+        return cls(wl.batch, wl.heads, wl.head_dim, wl.frames, wl.tokens_per_frame, wl.window,
+                   **kw)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib._lib is not None:
+            _lib._lib.sfa_generic_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def block_class(self, pass_: int, query_block: int, key_block: int) -> int:
+        c = ctypes.c_int32()
+        check(lib().sfa_generic_block_class(self._h, pass_, query_block, key_block,
+                                            ctypes.byref(c)), "sfa_generic_block_class")
+        return c.value
+
+    def workspace(self, device=None):
+        import torch
+
+        return torch.empty(self.info["workspace_bytes"], dtype=torch.uint8,
+                           device=device or "cuda")
+
+
+def sfa_generic_attention(plan: GenericPlan, q, k, v, out=None, workspace=None, stream=None):
+    """The generic two-pass ablation on one stream. Returns (out, workspace)."""
+    import torch
+
+    if workspace is None:
+        workspace = plan.workspace(q.device)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    check(lib().sfa_generic_attention(plan.handle, as_tensor(q, plan, "q"),
+                                      as_tensor(k, plan, "k"), as_tensor(v, plan, "v"),
+                                      as_tensor(out, plan, "o"),
+                                      ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                      _stream_ptr(stream)), "sfa_generic_attention")
+    return out, workspace
+
+
 # short aliases
 norms = sfa_norms
 fwd = sfa_fwd
@@ -220,3 +281,4 @@ attention_groups = sfa_attention_groups
 head_stats = sfa_read_head_stats
 row_norms = sfa_read_row_norms
 frame_stats = sfa_read_frame_stats
+generic_attention = sfa_generic_attention

@@ -188,9 +188,171 @@ NormParams norm_params(const sfa_plan* p, const sfa_tensor& q, const sfa_tensor&
   return n;
 }
 
+// Block class for the generic ablation: 0 empty, 1 full, 2 partial. Rows
+// [r0, r1) and keys [c0, c1) are the valid (unpadded) parts of the blocks; a
+// block with padded keys is never full (its padding must be masked).
+int generic_class(int pass, int r0, int r1, int c0, int c1, int T, int w) {
+  const bool whole = c1 - c0 == kGenericBk;
+  if (pass == 1) {  // reference-frame keys: every row sees them
+    if (c0 >= T) return 0;
+    return (c1 <= T && whole) ? 1 : 2;
+  }
+  const int fa = r0 / T, fb = (r1 - 1) / T, ga = c0 / T, gb = (c1 - 1) / T;
+  const int a0 = fa > 1 ? fa : 1, b0 = ga > 1 ? ga : 1;
+  if (a0 > fb || b0 > gb) return 0;                       // no video rows or keys
+  if (a0 > gb + w || b0 > fb + w) return 0;               // frame intervals too far apart
+  const bool all = fa >= 1 && ga >= 1 && whole && fb - ga <= w && gb - fa <= w;
+  return all ? 1 : 2;
+}
+
 }  // namespace
 
 extern "C" {
+
+int sfa_generic_create(const sfa_geometry* geom, sfa_generic** out) {
+  if (!out) return SFA_ERR_INVALID;
+  *out = nullptr;
+  int st = validate_geometry(geom);
+  if (st != SFA_OK) return st;
+  sfa_generic* g = new (std::nothrow) sfa_generic;
+  if (!g) return SFA_ERR_NOMEM;
+  memset(g, 0, sizeof(*g));
+  g->g = *geom;
+  const int T = geom->tokens_per_frame, F = geom->frames, w = geom->window;
+  const int D = geom->head_dim;
+  g->scale = geom->scale == 0.0f ? 1.0f / sqrtf(float(D)) : geom->scale;
+  g->S = (F + 1) * T;
+  g->nqb = (g->S + kGenericBq - 1) / kGenericBq;
+  g->nkb = (g->S + kGenericBk - 1) / kGenericBk;
+  g->offs = static_cast<int32_t*>(malloc(sizeof(int32_t) * 2 * (g->nqb + 1)));
+  // upper bound of the list length: every block of both passes
+  const size_t cap = size_t(2) * g->nqb * g->nkb;
+  g->lists = static_cast<int32_t*>(malloc(sizeof(int32_t) * (cap ? cap : 1)));
+  if (!g->offs || !g->lists) {
+    free(g->offs);
+    free(g->lists);
+    delete g;
+    return SFA_ERR_NOMEM;
+  }
+  int n = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int qb = 0; qb < g->nqb; ++qb) {
+      g->offs[pass * (g->nqb + 1) + qb] = n;
+      const int r0 = qb * kGenericBq, r1 = std::min(g->S, r0 + kGenericBq);
+      for (int kb = 0; kb < g->nkb; ++kb) {
+        const int c0 = kb * kGenericBk, c1 = std::min(g->S, c0 + kGenericBk);
+        const int cls = generic_class(pass, r0, r1, c0, c1, T, w);
+        if (cls == 0) continue;
+        g->lists[n++] = kb | (cls == 1 ? (1 << 30) : 0);
+        if (cls == 1) ++g->full_blocks; else ++g->partial_blocks;
+      }
+    }
+    g->offs[pass * (g->nqb + 1) + g->nqb] = n;
+  }
+  g->nlist = n;
+  const int64_t bh = int64_t(geom->batch) * geom->heads;
+  g->computed_pairs = (g->full_blocks + g->partial_blocks) * int64_t(kGenericBq) * kGenericBk * bh;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  g->ws_vt = take(size_t(bh) * D * size_t(g->S) * 2);
+  g->ws_lists = take(size_t(n ? n : 1) * 4);
+  g->ws_offs = take(size_t(2) * (g->nqb + 1) * 4);
+  g->ws_part = take(size_t(2) * bh * size_t(g->S) * D * 4);
+  g->ws_lse = take(size_t(2) * bh * size_t(g->S) * 4);
+  g->ws_total = off;
+  *out = g;
+  return SFA_OK;
+}
+
+void sfa_generic_destroy(sfa_generic* g) {
+  if (!g) return;
+  free(g->lists);
+  free(g->offs);
+  delete g;
+}
+
+int sfa_generic_get_info(const sfa_generic* g, sfa_generic_info* out) {
+  if (!g || !out) return SFA_ERR_INVALID;
+  out->block_q = kGenericBq;
+  out->block_k = kGenericBk;
+  out->query_blocks = g->nqb;
+  out->key_blocks = g->nkb;
+  out->full_blocks = g->full_blocks;
+  out->partial_blocks = g->partial_blocks;
+  out->computed_pairs = g->computed_pairs;
+  out->workspace_bytes = g->ws_total;
+  return SFA_OK;
+}
+
+int sfa_generic_block_class(const sfa_generic* g, int32_t pass, int32_t qb, int32_t kb,
+                            int32_t* cls) {
+  if (!g || !cls || pass < 0 || pass > 1 || qb < 0 || qb >= g->nqb || kb < 0 || kb >= g->nkb)
+    return SFA_ERR_INVALID;
+  *cls = 0;
+  for (int i = g->offs[pass * (g->nqb + 1) + qb]; i < g->offs[pass * (g->nqb + 1) + qb + 1]; ++i)
+    if ((g->lists[i] & ((1 << 30) - 1)) == kb) *cls = (g->lists[i] >> 30) ? 1 : 2;
+  return SFA_OK;
+}
+
+int sfa_generic_attention(const sfa_generic* g, sfa_tensor q, sfa_tensor k, sfa_tensor v,
+                          sfa_tensor o, void* ws, size_t ws_bytes, void* stream) {
+  if (!g || !ws) return SFA_ERR_INVALID;
+  if (ws_bytes < g->ws_total) return SFA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return SFA_ERR_UNSUPPORTED;
+  int st = check_tensor(q);
+  if (st == SFA_OK) st = check_tensor(k);
+  if (st == SFA_OK) st = check_tensor(v);
+  if (st == SFA_OK) st = check_tensor(o);
+  if (st != SFA_OK) return st;
+  // reuse the plan-based overlap test with a plan of the same geometry
+  sfa_plan tmp;
+  memset(&tmp, 0, sizeof(tmp));
+  tmp.g = g->g;
+  tmp.S = g->S;
+  if (ranges_overlap(&tmp, o, q) || ranges_overlap(&tmp, o, k) || ranges_overlap(&tmp, o, v))
+    return SFA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  hipError_t e = hipMemcpyAsync(base + g->ws_lists, g->lists, size_t(g->nlist) * 4,
+                                hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(base + g->ws_offs, g->offs, size_t(2) * (g->nqb + 1) * 4,
+                       hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_status(e);
+  NormParams n;
+  memset(&n, 0, sizeof(n));
+  n.v = static_cast<const uint16_t*>(v.data);
+  n.vsb = v.stride_b; n.vss = v.stride_s; n.vsh = v.stride_h;
+  n.vt = reinterpret_cast<uint16_t*>(base + g->ws_vt);
+  n.B = g->g.batch; n.H = g->g.heads; n.S = g->S; n.D = g->g.head_dim;
+  e = sfa_launch_vt(n, s);
+  if (e != hipSuccess) return hip_status(e);
+  GenericParams gp;
+  gp.q = static_cast<const uint16_t*>(q.data);
+  gp.k = static_cast<const uint16_t*>(k.data);
+  gp.qsb = q.stride_b; gp.qss = q.stride_s; gp.qsh = q.stride_h;
+  gp.ksb = k.stride_b; gp.kss = k.stride_s; gp.ksh = k.stride_h;
+  gp.vt = reinterpret_cast<const uint16_t*>(base + g->ws_vt);
+  gp.lists = reinterpret_cast<const int32_t*>(base + g->ws_lists);
+  gp.offs = reinterpret_cast<const int32_t*>(base + g->ws_offs);
+  gp.part = reinterpret_cast<float*>(base + g->ws_part);
+  gp.lse = reinterpret_cast<float*>(base + g->ws_lse);
+  gp.B = g->g.batch; gp.H = g->g.heads; gp.S = g->S; gp.T = g->g.tokens_per_frame;
+  gp.F = g->g.frames; gp.w = g->g.window; gp.nqb = g->nqb;
+  gp.items = 2 * g->g.batch * g->g.heads * g->nqb;
+  gp.c = g->scale * 1.4426950408889634f;
+  MergeParams m;
+  m.part = gp.part;
+  m.lse = gp.lse;
+  m.o = static_cast<uint16_t*>(o.data);
+  m.osb = o.stride_b; m.oss = o.stride_s; m.osh = o.stride_h;
+  m.B = g->g.batch; m.H = g->g.heads; m.S = g->S; m.D = g->g.head_dim;
+  return hip_status(sfa_launch_generic(gp, m, g->g.head_dim, s));
+}
 
 int sfa_plan_create(const sfa_geometry* geom, sfa_plan** out) {
   return create(geom, nullptr, out);

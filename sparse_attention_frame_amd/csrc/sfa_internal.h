@@ -134,7 +134,42 @@ struct NormParams {
   float bound_limit;
 };
 
+constexpr int kGenericBq = 256;  // ablation: query rows per block (8 waves x 32)
+constexpr int kGenericBk = 128;  // ablation: keys per block (2 LDS stages of 64)
+
+struct GenericParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t qsb, qss, qsh, ksb, kss, ksh;
+  const uint16_t* vt;     // [b][h][d][S]
+  const int32_t* lists;   // key blocks: kb | (full << 30), per (pass, query block)
+  const int32_t* offs;    // [2][nqb + 1] offsets into lists
+  float* part;            // [2][b][h][S][d] per-pass normalised outputs
+  float* lse;             // [2][b][h][S] per-pass log2-sum-exp2 of scale*log2(e)*s
+  int32_t B, H, S, T, F, w, nqb, items;
+  float c;                // scale * log2(e)
+};
+
+struct MergeParams {
+  const float* part;
+  const float* lse;
+  uint16_t* o;
+  int64_t osb, oss, osh;
+  int32_t B, H, S, D;
+};
+
 }  // namespace sfa
+
+struct sfa_generic {
+  sfa_geometry g;
+  float scale;
+  int32_t S, nqb, nkb;
+  int64_t full_blocks, partial_blocks, computed_pairs;
+  int32_t* lists;       // host copy, copied into the workspace on every call
+  int32_t nlist;
+  int32_t* offs;        // [2][nqb + 1]
+  size_t ws_vt, ws_lists, ws_offs, ws_part, ws_lse, ws_total;
+};
 
 struct sfa_plan {
   sfa_geometry g;
@@ -156,3 +191,6 @@ struct sfa_plan {
 hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream);
 hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, int waves, int stages,
                           hipStream_t stream);
+hipError_t sfa_launch_vt(const sfa::NormParams& p, hipStream_t stream);
+hipError_t sfa_launch_generic(const sfa::GenericParams& p, const sfa::MergeParams& m,
+                              int head_dim, hipStream_t stream);

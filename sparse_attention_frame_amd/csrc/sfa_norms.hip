@@ -290,6 +290,10 @@ hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(final_kernel, dim3(p.B * p.H), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return sfa_launch_vt(p, stream);
+}
+
+hipError_t sfa_launch_vt(const sfa::NormParams& p, hipStream_t stream) {
   const dim3 vgrid((p.S + 63) / 64, p.B * p.H);
   if (p.D == 128)
     hipLaunchKernelGGL(vt_kernel<128>, vgrid, dim3(256), 0, stream, p);

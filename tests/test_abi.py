@@ -230,3 +230,38 @@ def test_head_group_call_validation_happens_before_any_launch(L):
     mis = ctypes.c_void_p((1 << 20) + 16)
     assert G(p.handle, 2, t, t, t, t, mis, 2 * per, None, streams, 2) == \
         _lib.SFA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("F,T,w", [(4, 48, 1), (8, 208, 2), (3, 80, 5), (13, 32, 2), (0, 16, 0),
+                                   (6, 16, 1), (2, 400, 1)])
+def test_generic_blocks_match_the_oracle_mask(L, F, T, w):
+    """Ablation plan: every (pass, 256-row block, 128-key block) is classified exactly as the
+    oracle's mask says (window keys in pass 0, reference keys in pass 1), padding masked."""
+    from sparse_attention_frame_amd.api import GenericPlan
+
+    g = GenericPlan(1, 1, 64, F, T, w)
+    S = (F + 1) * T
+    mask = oracle.mask_matrix(F, T, w)
+    frame = np.arange(S) // T
+    info = g.info
+    assert info["query_blocks"] == -(-S // 256) and info["key_blocks"] == -(-S // 128)
+    full = partial = 0
+    for p in (0, 1):
+        pm = mask & ((frame[None, :] == 0) if p == 1 else (frame[None, :] >= 1))
+        for qb in range(info["query_blocks"]):
+            rows = slice(qb * 256, min(S, qb * 256 + 256))
+            for kb in range(info["key_blocks"]):
+                c0, c1 = kb * 128, min(S, kb * 128 + 128)
+                sub = pm[rows, c0:c1]
+                if not sub.any():
+                    want = 0
+                elif sub.all() and c1 - c0 == 128:
+                    want = 1
+                else:
+                    want = 2
+                assert g.block_class(p, qb, kb) == want, (p, qb, kb)
+                full += want == 1
+                partial += want == 2
+    assert (info["full_blocks"], info["partial_blocks"]) == (full, partial)
+    # the two passes cover the mask exactly once
+    assert not (mask & (frame[None, :] == 0) & (frame[None, :] >= 1)).any()
