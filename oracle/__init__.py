@@ -26,6 +26,9 @@ What it computes, in float64:
   query frame can see, and per-query-frame eligibility.
 * ``brute.attention_brute`` -- pure-Python loops over explicitly enumerated
   visible key sets (tiny inputs only).
+* ``prologue.qkv_prologue`` -- the attention's input chain (section "Layout as
+  ABI"): RMSNorm, the q/k/v projection, rotary embedding of q and k, head
+  packing; ``prologue.rms_norm`` and ``prologue.rotate_pairs`` are its steps.
 
 Pins (``tests/test_oracle.py``, all CPU): brute force, torch's fp64
 scaled-dot-product attention with an independently built mask, closed-form
@@ -46,3 +49,4 @@ from .attention import (  # noqa: F401
     row_offsets,
 )
 from .brute import attention_brute  # noqa: F401
+from .prologue import qkv_prologue, rms_norm, rotate_pairs  # noqa: F401

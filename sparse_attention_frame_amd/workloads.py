@@ -93,3 +93,69 @@ def make_inputs(wl: Workload):
     import torch
 
     return tuple(torch.from_numpy(x).to(torch.bfloat16) for x in make_inputs_np(wl))
+
+
+# ---- inputs of the fused attention prologue (RMSNorm -> projection -> rotary -> packing) ----
+
+@dataclass(frozen=True)
+class PrologueWorkload:
+    name: str
+    frames: int            # F video frames (+ the reference frame)
+    grid_h: int            # latent patch grid of one frame: T = grid_h * grid_w tokens
+    grid_w: int
+    heads: int
+    head_dim: int
+    model_dim: int         # C, the width of the hidden states
+    seed: int
+    batch: int = 1
+
+    @property
+    def tokens_per_frame(self) -> int:
+        return self.grid_h * self.grid_w
+
+    @property
+    def seq(self) -> int:
+        return (self.frames + 1) * self.tokens_per_frame
+
+
+PRO_TINY = PrologueWorkload("pro_tiny", frames=4, grid_h=6, grid_w=8, heads=2, head_dim=64,
+                            model_dim=128, seed=2000)
+PRO_SMALL = PrologueWorkload("pro_small", frames=8, grid_h=13, grid_w=16, heads=8, head_dim=128,
+                             model_dim=1024, seed=2001)
+PRO_720P = PrologueWorkload("pro_720p", frames=13, grid_h=45, grid_w=80, heads=12, head_dim=128,
+                            model_dim=1536, seed=2002)
+PROLOGUE = {w.name: w for w in (PRO_TINY, PRO_SMALL, PRO_720P)}
+
+
+def rope_tables(pw: PrologueWorkload, base: float = 10000.0):
+    """cos, sin [S, d/2] float32 for 3-axis positions (frame, row, column) of every token:
+    the d/2 rotation pairs are split over the three axes (a quarter each for the frame
+    axis, the rest halved between rows and columns), frequencies base^(-i/n) per axis.
+    The reference frame has frame position 0, video frame f position f."""
+    half = pw.head_dim // 2
+    nt = half // 4
+    nh = (half - nt) // 2
+    nw = half - nt - nh
+    T = pw.tokens_per_frame
+    tok = np.arange(pw.seq)
+    pos = np.stack([tok // T, (tok % T) // pw.grid_w, tok % pw.grid_w], axis=1).astype(np.float64)
+    ang = []
+    for axis, n in enumerate((nt, nh, nw)):
+        freq = base ** (-np.arange(n) / n)
+        ang.append(pos[:, axis:axis + 1] * freq[None, :])
+    ang = np.concatenate(ang, axis=1)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def make_prologue_inputs_np(pw: PrologueWorkload):
+    """x [B, S, C], gamma [C], w [3*H*d, C] (bf16-representable float32) and the rope tables."""
+    import torch
+
+    rng = np.random.default_rng(pw.seed)
+    C, N = pw.model_dim, 3 * pw.heads * pw.head_dim
+    x = rng.standard_normal((pw.batch, pw.seq, C), dtype=np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(C)).astype(np.float32)
+    w = (rng.standard_normal((N, C)) / np.sqrt(C)).astype(np.float32)
+    out = [torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy() for a in (x, gamma, w)]
+    cos, sin = rope_tables(pw)
+    return (*out, cos, sin)
