@@ -192,6 +192,40 @@ int sfa_read_row_norms(const sfa_plan* plan, const void* workspace, float* qnorm
 int sfa_read_frame_stats(const sfa_plan* plan, const void* workspace, float* kvis, float* bound,
                          uint8_t* eligible, void* stream);
 
+/* ---- Fused attention prologue (section "Layout as ABI", Fig. 5) ----
+ * The chain that produces the attention's inputs -- normalisation, projection,
+ * rotary embedding, head packing -- as one MFMA kernel that writes q, k, v
+ * straight into the sfa_tensor layout sfa_norms / sfa_fwd read:
+ *   xn = x / sqrt(mean_c x^2 + eps) * gamma          (RMSNorm over C)
+ *   [q | k | v] = xn . W^T,  W stored [3*H*d][C]     (row n: tensor n / (H*d),
+ *                                                     head (n / d) % H, element n % d)
+ *   q, k: pairs (e, e + d/2), e < d/2, rotated by cos[s][e], sin[s][e].
+ * gamma is folded into W once (sfa_prologue_fold); the kernel scales each
+ * token's outputs by its inverse RMS. bf16 in and out, fp32 accumulation. */
+typedef struct sfa_prologue_geometry {
+  int32_t batch;
+  int32_t seq;        /* S tokens per batch entry */
+  int32_t model_dim;  /* C: a multiple of 64 */
+  int32_t heads;      /* H; heads * head_dim must be a multiple of 256 */
+  int32_t head_dim;   /* 64 or 128 */
+  float eps;          /* RMSNorm epsilon, >= 0 */
+} sfa_prologue_geometry;
+
+/* W' = bf16(gamma[c] * W[n][c]) for bf16 W [rows][cols] and gamma [cols] (device
+ * pointers, 16-byte aligned, cols even). Run once per weight. */
+int sfa_prologue_fold(const void* w, const void* gamma, void* w_folded, int32_t rows,
+                      int32_t cols, void* stream);
+/* Device workspace of sfa_qkv_prologue: B * S floats (per-token inverse RMS). */
+int sfa_prologue_workspace_bytes(const sfa_prologue_geometry* geom, size_t* bytes);
+/* x: bf16 [B][S][C] (stride_b, stride_s in elements, C contiguous, stride_s <= 2^22;
+ * stride_h ignored). w_folded: bf16 [3*H*d][C] from sfa_prologue_fold. cos, sin:
+ * fp32 [S][d/2]. q, k, v: bf16 [B][S][H][d] in any sfa_tensor strides (they must
+ * not overlap x). Two launches on `stream`: the inverse-RMS pass, then the fused
+ * projection. SFA_ERR_UNSUPPORTED for shapes outside the rules above. */
+int sfa_qkv_prologue(const sfa_prologue_geometry* geom, sfa_tensor x, const void* w_folded,
+                     const float* cos_table, const float* sin_table, sfa_tensor q, sfa_tensor k,
+                     sfa_tensor v, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- Ablation: generic block-sparse attention (measured, not the product path) ----
  * The design the pages started from (section "Deleting the mask": splash-style
  * block-sparse attention with generic tile sizes that ignore frame

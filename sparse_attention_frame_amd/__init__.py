@@ -16,12 +16,16 @@ from .api import (  # noqa: F401
     generic_attention,
     head_stats,
     norms,
+    prologue_fold,
+    qkv_prologue,
     row_norms,
     sfa_attention,
     sfa_attention_groups,
     sfa_fwd,
     sfa_generic_attention,
     sfa_norms,
+    sfa_prologue_fold,
+    sfa_qkv_prologue,
     sfa_read_frame_stats,
     sfa_read_head_stats,
     sfa_read_row_norms,

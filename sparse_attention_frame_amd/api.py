@@ -13,7 +13,8 @@ import ctypes
 import numpy as np
 
 from . import _lib
-from ._lib import GenericInfo, Geometry, PlanInfo, PlanOptions, Tensor, check, lib
+from ._lib import (GenericInfo, Geometry, PlanInfo, PlanOptions, PrologueGeometry, Tensor,
+                   check, lib)
 
 
 def _stream_ptr(stream):
@@ -212,6 +213,61 @@ def sfa_read_frame_stats(plan: Plan, workspace, stream=None):
     return {"kvis": kvis, "bound": bound, "eligible": elig.astype(bool)}
 
 
+def sfa_prologue_fold(w, gamma, stream=None):
+    """W' = bf16(gamma * W) for bf16 device tensors W [N, C], gamma [C]."""
+    import torch
+
+    if w.dtype != torch.bfloat16 or gamma.dtype != torch.bfloat16 or w.dim() != 2 or \
+            not w.is_contiguous() or tuple(gamma.shape) != (w.shape[1],):
+        raise ValueError("w must be a contiguous bf16 [N, C] tensor and gamma bf16 [C]")
+    out = torch.empty_like(w)
+    check(lib().sfa_prologue_fold(ctypes.c_void_p(w.data_ptr()),
+                                  ctypes.c_void_p(gamma.contiguous().data_ptr()),
+                                  ctypes.c_void_p(out.data_ptr()), w.shape[0], w.shape[1],
+                                  _stream_ptr(stream)), "sfa_prologue_fold")
+    return out
+
+
+def sfa_qkv_prologue(x, w_folded, cos, sin, heads: int, head_dim: int, eps: float = 1e-6,
+                     q=None, k=None, v=None, workspace=None, stream=None):
+    """Fused RMSNorm -> projection -> rotary -> head packing. x bf16 [B, S, C] (C
+    contiguous), w_folded bf16 [3*H*d, C], cos/sin float32 [S, d/2]. Returns (q, k, v),
+    bf16 [B, S, H, d] (or the given output tensors, any strides with d contiguous)."""
+    import torch
+
+    B, S, C = x.shape
+    if x.dtype != torch.bfloat16 or x.stride(2) != 1:
+        raise ValueError("x must be bf16 [B, S, C] with C contiguous")
+    if w_folded.dtype != torch.bfloat16 or tuple(w_folded.shape) != (3 * heads * head_dim, C) \
+            or not w_folded.is_contiguous():
+        raise ValueError("w_folded must be a contiguous bf16 [3*H*d, C] tensor")
+    for t in (cos, sin):
+        if t.dtype != torch.float32 or tuple(t.shape) != (S, head_dim // 2) or \
+                not t.is_contiguous():
+            raise ValueError("cos / sin must be contiguous float32 [S, d/2]")
+    g = PrologueGeometry(B, S, C, heads, head_dim, eps)
+    outs = []
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is None:
+            t = torch.empty((B, S, heads, head_dim), dtype=torch.bfloat16, device=x.device)
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, S, heads, head_dim) or \
+                t.stride(3) != 1:
+            raise ValueError(f"{name} must be bf16 [B, S, H, d] with d contiguous")
+        outs.append(t)
+    if workspace is None:
+        n = ctypes.c_size_t()
+        check(lib().sfa_prologue_workspace_bytes(ctypes.byref(g), ctypes.byref(n)),
+              "sfa_prologue_workspace_bytes")
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=x.device)
+    xt = Tensor(x.data_ptr(), x.stride(0), x.stride(1), 0)
+    ts = [Tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2)) for t in outs]
+    check(lib().sfa_qkv_prologue(ctypes.byref(g), xt, ctypes.c_void_p(w_folded.data_ptr()),
+                                 ctypes.c_void_p(cos.data_ptr()), ctypes.c_void_p(sin.data_ptr()),
+                                 *ts, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                 _stream_ptr(stream)), "sfa_qkv_prologue")
+    return tuple(outs)
+
+
 class GenericPlan:
     """Ablation (sfa_generic_create): generic 256 x 128 block-sparse tiles, element masks on
     partial blocks, window and reference-frame keys as two passes plus a merge."""
@@ -282,3 +338,5 @@ head_stats = sfa_read_head_stats
 row_norms = sfa_read_row_norms
 frame_stats = sfa_read_frame_stats
 generic_attention = sfa_generic_attention
+prologue_fold = sfa_prologue_fold
+qkv_prologue = sfa_qkv_prologue

@@ -205,9 +205,93 @@ int generic_class(int pass, int r0, int r1, int c0, int c1, int T, int w) {
   return all ? 1 : 2;
 }
 
+int validate_prologue(const sfa_prologue_geometry* g) {
+  if (!g) return SFA_ERR_INVALID;
+  if (g->batch < 1 || g->seq < 1 || g->model_dim < 1 || g->heads < 1) return SFA_ERR_INVALID;
+  if (!(g->eps >= 0.0f) || !isfinite(g->eps)) return SFA_ERR_INVALID;
+  if (g->head_dim != 64 && g->head_dim != 128) return SFA_ERR_UNSUPPORTED;
+  if (g->model_dim % kProKStage != 0) return SFA_ERR_UNSUPPORTED;
+  if ((int64_t(g->heads) * g->head_dim) % kProTile != 0) return SFA_ERR_UNSUPPORTED;
+  const int64_t N = 3 * int64_t(g->heads) * g->head_dim;
+  // 32-bit offsets: W' rows of one tile, tokens, feature and tile counts
+  if (N * g->model_dim * 2 > (int64_t(1) << 31) - 1) return SFA_ERR_UNSUPPORTED;
+  if (int64_t(g->batch) * g->seq > (int64_t(1) << 30)) return SFA_ERR_UNSUPPORTED;
+  return SFA_OK;
+}
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 }  // namespace
 
 extern "C" {
+
+int sfa_prologue_fold(const void* w, const void* gamma, void* w_folded, int32_t rows, int32_t cols,
+                      void* stream) {
+  if (!w || !gamma || !w_folded || rows < 1 || cols < 2) return SFA_ERR_INVALID;
+  if (cols % 2 != 0 || !aligned16(w) || !aligned16(gamma) || !aligned16(w_folded))
+    return SFA_ERR_UNSUPPORTED;
+  return hip_status(sfa_launch_fold(static_cast<const uint16_t*>(w),
+                                    static_cast<const uint16_t*>(gamma),
+                                    static_cast<uint16_t*>(w_folded), rows, cols,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int sfa_prologue_workspace_bytes(const sfa_prologue_geometry* g, size_t* bytes) {
+  if (!bytes) return SFA_ERR_INVALID;
+  const int st = validate_prologue(g);
+  if (st != SFA_OK) return st;
+  *bytes = align256(size_t(g->batch) * g->seq * 4);
+  return SFA_OK;
+}
+
+int sfa_qkv_prologue(const sfa_prologue_geometry* g, sfa_tensor x, const void* w,
+                     const float* cosv, const float* sinv, sfa_tensor q, sfa_tensor k, sfa_tensor v,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int st = validate_prologue(g);
+  if (st != SFA_OK) return st;
+  if (!w || !cosv || !sinv || !ws || !x.data) return SFA_ERR_INVALID;
+  if (ws_bytes < size_t(g->batch) * g->seq * 4) return SFA_ERR_INVALID;
+  if (!aligned16(w) || !aligned16(cosv) || !aligned16(sinv) || !aligned16(x.data) ||
+      (reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+    return SFA_ERR_UNSUPPORTED;
+  if (x.stride_b < 0 || x.stride_s < g->model_dim) return SFA_ERR_INVALID;
+  if ((x.stride_b | x.stride_s) & 7) return SFA_ERR_UNSUPPORTED;
+  if (x.stride_s > (int64_t(1) << 22)) return SFA_ERR_UNSUPPORTED;
+  st = check_tensor(q);
+  if (st == SFA_OK) st = check_tensor(k);
+  if (st == SFA_OK) st = check_tensor(v);
+  if (st != SFA_OK) return st;
+  // the outputs may not overlap the input
+  auto overlaps_x = [&](const sfa_tensor& o) {
+    const uintptr_t xlo = reinterpret_cast<uintptr_t>(x.data);
+    const uintptr_t xhi = xlo + uintptr_t(int64_t(g->batch - 1) * x.stride_b +
+                                          int64_t(g->seq - 1) * x.stride_s + g->model_dim) * 2;
+    const uintptr_t olo = reinterpret_cast<uintptr_t>(o.data);
+    const uintptr_t ohi = olo + uintptr_t(int64_t(g->batch - 1) * o.stride_b +
+                                          int64_t(g->seq - 1) * o.stride_s +
+                                          int64_t(g->heads - 1) * o.stride_h + g->head_dim) * 2;
+    return olo < xhi && xlo < ohi;
+  };
+  if (overlaps_x(q) || overlaps_x(k) || overlaps_x(v)) return SFA_ERR_INVALID;
+  ProParams p;
+  p.x = static_cast<const uint16_t*>(x.data);
+  p.xsb = x.stride_b;
+  p.xss = x.stride_s;
+  p.w = static_cast<const uint16_t*>(w);
+  p.cosv = cosv;
+  p.sinv = sinv;
+  p.rstd = static_cast<float*>(ws);
+  const sfa_tensor* outs[3] = {&q, &k, &v};
+  for (int i = 0; i < 3; ++i) {
+    p.out[i] = static_cast<uint16_t*>(outs[i]->data);
+    p.osb[i] = outs[i]->stride_b;
+    p.oss[i] = outs[i]->stride_s;
+    p.osh[i] = outs[i]->stride_h;
+  }
+  p.B = g->batch; p.S = g->seq; p.C = g->model_dim; p.H = g->heads; p.d = g->head_dim;
+  p.ntile_f = 3 * g->heads * g->head_dim / kProTile;
+  p.ntile_t = (g->seq + kProTile - 1) / kProTile;
+  p.eps = g->eps;
+  return hip_status(sfa_launch_prologue(p, static_cast<hipStream_t>(stream)));
+}
 
 int sfa_generic_create(const sfa_geometry* geom, sfa_generic** out) {
   if (!out) return SFA_ERR_INVALID;

@@ -158,6 +158,27 @@ struct MergeParams {
   int32_t B, H, S, D;
 };
 
+// Fused prologue: D[feature][token] = W'[feature][:] . x[token][:] on 256 x 256
+// workgroup tiles, scaled by the token's inverse RMS, rotated (q, k) and stored
+// into q, k, v [b][s][h][e].
+constexpr int kProTile = 256;   // features and tokens per workgroup tile
+constexpr int kProKStage = 64;  // model-width elements per LDS stage
+
+struct ProParams {
+  const uint16_t* x;      // [b][s][C], C contiguous
+  int64_t xsb, xss;       // element strides
+  const uint16_t* w;      // W' = gamma * W, [3*H*d][C] bf16
+  const float* cosv;      // [S][d/2]
+  const float* sinv;
+  float* rstd;            // [B][S] workspace
+  uint16_t* out[3];       // q, k, v
+  int64_t osb[3], oss[3], osh[3];
+  int32_t B, S, C, H, d;
+  int32_t ntile_f;        // 3*H*d / 256
+  int32_t ntile_t;        // ceil(S / 256) per batch
+  float eps;
+};
+
 }  // namespace sfa
 
 struct sfa_generic {
@@ -192,5 +213,8 @@ hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream);
 hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, int waves, int stages,
                           hipStream_t stream);
 hipError_t sfa_launch_vt(const sfa::NormParams& p, hipStream_t stream);
+hipError_t sfa_launch_fold(const uint16_t* w, const uint16_t* gamma, uint16_t* out, int rows,
+                           int cols, hipStream_t stream);
+hipError_t sfa_launch_prologue(const sfa::ProParams& p, hipStream_t stream);
 hipError_t sfa_launch_generic(const sfa::GenericParams& p, const sfa::MergeParams& m,
                               int head_dim, hipStream_t stream);

@@ -118,8 +118,8 @@ class PrologueWorkload:
         return (self.frames + 1) * self.tokens_per_frame
 
 
-PRO_TINY = PrologueWorkload("pro_tiny", frames=4, grid_h=6, grid_w=8, heads=2, head_dim=64,
-                            model_dim=128, seed=2000)
+PRO_TINY = PrologueWorkload("pro_tiny", frames=4, grid_h=6, grid_w=8, heads=4, head_dim=64,
+                            model_dim=256, seed=2000)
 PRO_SMALL = PrologueWorkload("pro_small", frames=8, grid_h=13, grid_w=16, heads=8, head_dim=128,
                              model_dim=1024, seed=2001)
 PRO_720P = PrologueWorkload("pro_720p", frames=13, grid_h=45, grid_w=80, heads=12, head_dim=128,

@@ -265,3 +265,69 @@ def test_generic_blocks_match_the_oracle_mask(L, F, T, w):
     assert (info["full_blocks"], info["partial_blocks"]) == (full, partial)
     # the two passes cover the mask exactly once
     assert not (mask & (frame[None, :] == 0) & (frame[None, :] >= 1)).any()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), _lib.SFA_ERR_UNSUPPORTED),
+    (dict(model_dim=100), _lib.SFA_ERR_UNSUPPORTED),
+    (dict(heads=3, head_dim=64), _lib.SFA_ERR_UNSUPPORTED),      # H*d not a multiple of 256
+    (dict(eps=-1.0), _lib.SFA_ERR_INVALID),
+    (dict(eps=float("nan")), _lib.SFA_ERR_INVALID),
+    (dict(batch=0), _lib.SFA_ERR_INVALID),
+    (dict(seq=0), _lib.SFA_ERR_INVALID),
+    (dict(heads=0), _lib.SFA_ERR_INVALID),
+    (dict(heads=128, head_dim=128, model_dim=65536), _lib.SFA_ERR_UNSUPPORTED),  # W' > 2 GiB
+])
+def test_prologue_geometry_errors(L, kw, status):
+    base = dict(batch=1, seq=100, model_dim=256, heads=4, head_dim=64, eps=1e-6)
+    base.update(kw)
+    g = _lib.PrologueGeometry(base["batch"], base["seq"], base["model_dim"], base["heads"],
+                              base["head_dim"], base["eps"])
+    n = ctypes.c_size_t()
+    assert L.sfa_prologue_workspace_bytes(ctypes.byref(g), ctypes.byref(n)) == status
+
+
+def test_prologue_workspace_is_one_float_per_token(L):
+    for B, S in [(1, 100), (2, 50400), (3, 1)]:
+        g = _lib.PrologueGeometry(B, S, 1536, 12, 128, 1e-6)
+        n = ctypes.c_size_t()
+        assert L.sfa_prologue_workspace_bytes(ctypes.byref(g), ctypes.byref(n)) == 0
+        assert n.value >= 4 * B * S and n.value % 256 == 0 and n.value - 4 * B * S < 256
+    assert L.sfa_prologue_workspace_bytes(None, ctypes.byref(n)) == _lib.SFA_ERR_INVALID
+
+
+def test_prologue_call_validation_happens_before_any_launch(L):
+    """sfa_prologue_fold / sfa_qkv_prologue reject bad arguments without touching the GPU."""
+    P = ctypes.c_void_p
+    fold = L.sfa_prologue_fold
+    assert fold(None, P(4096), P(8192), 16, 64, None) == _lib.SFA_ERR_INVALID
+    assert fold(P(4096), P(8192), P(1 << 20), 0, 64, None) == _lib.SFA_ERR_INVALID
+    assert fold(P(4096), P(8192), P(1 << 20), 16, 63, None) == _lib.SFA_ERR_UNSUPPORTED
+    assert fold(P(4096 + 2), P(8192), P(1 << 20), 16, 64, None) == _lib.SFA_ERR_UNSUPPORTED
+
+    B, S, C, H, d = 1, 100, 256, 4, 64
+    g = _lib.PrologueGeometry(B, S, C, H, d, 1e-6)
+    x = _lib.Tensor(1 << 20, S * C, C, 0)
+    w, cs, sn = P(1 << 22), P(1 << 23), P(1 << 24)
+    outs = [_lib.Tensor((1 << 26) * (i + 1), S * H * d, H * d, d) for i in range(3)]
+    ws, need = P(1 << 25), 4 * B * S
+    Q = L.sfa_qkv_prologue
+    assert Q(None, x, w, cs, sn, *outs, ws, need, None) == _lib.SFA_ERR_INVALID
+    assert Q(ctypes.byref(g), x, None, cs, sn, *outs, ws, need, None) == _lib.SFA_ERR_INVALID
+    assert Q(ctypes.byref(g), x, w, None, sn, *outs, ws, need, None) == _lib.SFA_ERR_INVALID
+    assert Q(ctypes.byref(g), x, w, cs, sn, *outs, None, need, None) == _lib.SFA_ERR_INVALID
+    assert Q(ctypes.byref(g), x, w, cs, sn, *outs, ws, need - 1, None) == _lib.SFA_ERR_INVALID
+    assert Q(ctypes.byref(g), x, w, cs, sn, *outs, P((1 << 25) + 16), need, None) == \
+        _lib.SFA_ERR_UNSUPPORTED
+    assert Q(ctypes.byref(g), x, P((1 << 22) + 8), cs, sn, *outs, ws, need, None) == \
+        _lib.SFA_ERR_UNSUPPORTED
+    assert Q(ctypes.byref(g), _lib.Tensor(1 << 20, S * C, C - 8, 0), w, cs, sn, *outs, ws, need,
+             None) == _lib.SFA_ERR_INVALID                        # rows overlap
+    assert Q(ctypes.byref(g), _lib.Tensor(1 << 20, S * C, C + 4, 0), w, cs, sn, *outs, ws, need,
+             None) == _lib.SFA_ERR_UNSUPPORTED                    # row stride not 16-byte
+    bad_out = _lib.Tensor(1 << 26, S * H * d, H * d + 2, d)
+    assert Q(ctypes.byref(g), x, w, cs, sn, bad_out, outs[1], outs[2], ws, need, None) == \
+        _lib.SFA_ERR_UNSUPPORTED
+    on_x = _lib.Tensor((1 << 20) + 64, S * H * d, H * d, d)       # output aliasing x
+    assert Q(ctypes.byref(g), x, w, cs, sn, outs[0], on_x, outs[2], ws, need, None) == \
+        _lib.SFA_ERR_INVALID
