@@ -85,6 +85,116 @@ def cpu_baseline(wl, q_np, k_np, v_np, budget_s=12.0):
                       f"fp64 dense-masked numpy, {dt:.1f} s"}
 
 
+def cpu_baseline_prologue(pw, x, gamma, w, cos, sin, budget_s=12.0):
+    """Time the oracle prologue on chunks of 512 tokens until ~budget_s; TFLOP/s."""
+    import numpy as np
+
+    import oracle
+
+    flops_tok = 2.0 * pw.model_dim * 3 * pw.heads * pw.head_dim
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < pw.seq:
+        sl = slice(done, min(done + 512, pw.seq))
+        oracle.qkv_prologue(x[:, sl], gamma, w, cos[sl], sin[sl], pw.heads, pw.head_dim)
+        done = sl.stop
+    el = time.perf_counter() - t0
+    return {"value": round(done * pw.batch * flops_tok / el / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+            "kind": "oracle",
+            "sample": f"first {done} tokens of batch 0 in 512-token chunks, fp64, {el:.1f} s"}
+
+
+def bench_prologue(args):
+    """Fused prologue at the 720p layer's shape: x [1, 50400, 1536] bf16 -> q, k, v
+    [1, 50400, 12, 128]. value = 2 * S * C * 3Hd flops / time of one sfa_qkv_prologue call
+    (one kernel); the unfused PyTorch chain and torch's bare projection GEMM are timed
+    beside."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_frame_amd as sfa
+    from sparse_attention_frame_amd import workloads as W
+
+    pw = W.PRO_720P
+    log(f"bench: generating {pw.name} inputs")
+    x_np, g_np, w_np, cos_np, sin_np = W.make_prologue_inputs_np(pw)
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    x, gamma, w = bf(x_np), bf(g_np), bf(w_np)
+    cos, sin = (torch.from_numpy(a).to(dev) for a in (cos_np, sin_np))
+    stream = torch.cuda.current_stream()
+    H, d, B, S, C = pw.heads, pw.head_dim, pw.batch, pw.seq, pw.model_dim
+    wf = sfa.prologue_fold(w, gamma, stream=stream)
+    q, k, v = sfa.qkv_prologue(x, wf, cos, sin, H, d, stream=stream)
+    def step():
+        sfa.qkv_prologue(x, wf, cos, sin, H, d, q=q, k=k, v=v, stream=stream)
+
+    def unfused():
+        xn = torch.nn.functional.rms_norm(x.float(), (C,), gamma.float(), 1e-6).to(torch.bfloat16)
+        y = torch.nn.functional.linear(xn, w).view(B, S, 3, H, d)
+        c, s_ = cos[None, :, None, :], sin[None, :, None, :]
+        outs = []
+        for i in range(3):
+            u = y[:, :, i].float()
+            if i < 2:
+                a, b = u[..., :d // 2], u[..., d // 2:]
+                u = torch.cat([a * c - b * s_, a * s_ + b * c], dim=-1)
+            outs.append(u.to(torch.bfloat16).contiguous())
+        return outs
+
+    def timed(fn, n):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e in ev:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n, [a.elapsed_time(b) for a, b in ev]
+
+    log("bench: warmup")
+    for _ in range(args.warmup):
+        step()
+        unfused()
+    log(f"bench: timing {args.steps} prologue calls")
+    ms_step, ev_ms = timed(step, args.steps)
+    un_ms, un_ev = timed(unfused, max(5, args.steps // 5))
+    _, lin_ev = timed(lambda: torch.nn.functional.linear(x, w), max(5, args.steps // 5))
+    ref = unfused()
+    err = max(float((a.float() - b.float()).abs().max()) for a, b in zip((q, k, v), ref))
+    flops = 2.0 * B * S * C * 3 * H * d
+    kern_ms = float(np.mean(ev_ms))
+    res = {
+        "metric": "fused q/k/v prologue TFLOP/s on 1 MI355X; % of bf16 MFMA peak",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"720p-shaped layer prologue: x [{B}, {S}, {C}] -> q, k, v "
+                               f"[{B}, {S}, {H}, {d}] (RMSNorm, projection, 3-axis rotary, "
+                               "head packing)",
+                   "gflop": round(flops / 1e9, 1)},
+        "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "call_ms": round(kern_ms, 4), "call_min_ms": round(float(np.min(ev_ms)), 4),
+        "unfused_torch_ms": round(float(np.mean(un_ev)), 4),
+        "torch_linear_ms": round(float(np.mean(lin_ev)), 4),
+        "max_abs_vs_unfused_torch": round(err, 5),
+        "roofline": {"bound": "mfma", "kernel": "prologue_kernel (sfa_qkv_prologue is one "
+                                                "launch)",
+                     "achieved": round(flops / (kern_ms * 1e-3) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline_prologue(pw, x_np, g_np, w_np, cos_np, sin_np)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +213,9 @@ def main():
                     help="streams the head groups are spread over (0: the current stream)")
     ap.add_argument("--ablation", choices=["none", "generic"], default="none",
                     help="generic: time the generic block-sparse two-pass ablation instead")
+    ap.add_argument("--prologue", action="store_true",
+                    help="time the fused q/k/v prologue (RMSNorm, projection, rotary, packing) "
+                         "at the 720p layer's shape instead of the attention")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one elementwise copy of this size (calibrates HBM counters)")
     args = ap.parse_args()
@@ -110,6 +223,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.prologue:
+        bench_prologue(args)
+        return
 
     import numpy as np
     import torch

@@ -200,8 +200,9 @@ int sfa_read_frame_stats(const sfa_plan* plan, const void* workspace, float* kvi
  *   [q | k | v] = xn . W^T,  W stored [3*H*d][C]     (row n: tensor n / (H*d),
  *                                                     head (n / d) % H, element n % d)
  *   q, k: pairs (e, e + d/2), e < d/2, rotated by cos[s][e], sin[s][e].
- * gamma is folded into W once (sfa_prologue_fold); the kernel scales each
- * token's outputs by its inverse RMS. bf16 in and out, fp32 accumulation. */
+ * gamma is folded into W once (sfa_prologue_fold); the kernel sums each token's
+ * squares from the x operands it stages anyway and scales the token's outputs by
+ * the inverse RMS. bf16 in and out, fp32 accumulation, no workspace. */
 typedef struct sfa_prologue_geometry {
   int32_t batch;
   int32_t seq;        /* S tokens per batch entry */
@@ -215,16 +216,15 @@ typedef struct sfa_prologue_geometry {
  * pointers, 16-byte aligned, cols even). Run once per weight. */
 int sfa_prologue_fold(const void* w, const void* gamma, void* w_folded, int32_t rows,
                       int32_t cols, void* stream);
-/* Device workspace of sfa_qkv_prologue: B * S floats (per-token inverse RMS). */
-int sfa_prologue_workspace_bytes(const sfa_prologue_geometry* geom, size_t* bytes);
 /* x: bf16 [B][S][C] (stride_b, stride_s in elements, C contiguous, stride_s <= 2^22;
  * stride_h ignored). w_folded: bf16 [3*H*d][C] from sfa_prologue_fold. cos, sin:
  * fp32 [S][d/2]. q, k, v: bf16 [B][S][H][d] in any sfa_tensor strides (they must
- * not overlap x). Two launches on `stream`: the inverse-RMS pass, then the fused
- * projection. SFA_ERR_UNSUPPORTED for shapes outside the rules above. */
+ * not overlap x). One launch on `stream`. Returns SFA_ERR_INVALID for null or
+ * overlapping arguments, SFA_ERR_UNSUPPORTED for shapes, strides or alignments
+ * outside the rules above (data pointers 16-byte aligned, strides multiples of 8). */
 int sfa_qkv_prologue(const sfa_prologue_geometry* geom, sfa_tensor x, const void* w_folded,
                      const float* cos_table, const float* sin_table, sfa_tensor q, sfa_tensor k,
-                     sfa_tensor v, void* workspace, size_t workspace_bytes, void* stream);
+                     sfa_tensor v, void* stream);
 
 /* ---- Ablation: generic block-sparse attention (measured, not the product path) ----
  * The design the pages started from (section "Deleting the mask": splash-style

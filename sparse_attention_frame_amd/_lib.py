@@ -57,7 +57,7 @@ EXPORTS = (
     "sfa_plan_create", "sfa_plan_create_ex", "sfa_plan_destroy", "sfa_plan_get_info",
     "sfa_plan_key_ranges", "sfa_plan_item", "sfa_norms", "sfa_fwd", "sfa_attention",
     "sfa_attention_groups", "sfa_read_head_stats", "sfa_read_row_norms", "sfa_read_frame_stats",
-    "sfa_prologue_fold", "sfa_prologue_workspace_bytes", "sfa_qkv_prologue",
+    "sfa_prologue_fold", "sfa_qkv_prologue",
     "sfa_generic_create", "sfa_generic_destroy", "sfa_generic_get_info", "sfa_generic_block_class",
     "sfa_generic_attention", "sfa_status_str",
 )
@@ -96,10 +96,8 @@ def _declare(lib):
         "sfa_read_row_norms": (ctypes.c_int, [P, P, f32p, f32p, P]),
         "sfa_read_frame_stats": (ctypes.c_int, [P, P, f32p, f32p, u8p, P]),
         "sfa_prologue_fold": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32, P]),
-        "sfa_prologue_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(PrologueGeometry),
-                                                        ctypes.POINTER(ctypes.c_size_t)]),
         "sfa_qkv_prologue": (ctypes.c_int, [ctypes.POINTER(PrologueGeometry), Tensor, P, P, P,
-                                            Tensor, Tensor, Tensor, P, ctypes.c_size_t, P]),
+                                            Tensor, Tensor, Tensor, P]),
         "sfa_generic_create": (ctypes.c_int, [ctypes.POINTER(Geometry), ctypes.POINTER(P)]),
         "sfa_generic_destroy": (None, [P]),
         "sfa_generic_get_info": (ctypes.c_int, [P, ctypes.POINTER(GenericInfo)]),

@@ -229,7 +229,7 @@ def sfa_prologue_fold(w, gamma, stream=None):
 
 
 def sfa_qkv_prologue(x, w_folded, cos, sin, heads: int, head_dim: int, eps: float = 1e-6,
-                     q=None, k=None, v=None, workspace=None, stream=None):
+                     q=None, k=None, v=None, stream=None):
     """Fused RMSNorm -> projection -> rotary -> head packing. x bf16 [B, S, C] (C
     contiguous), w_folded bf16 [3*H*d, C], cos/sin float32 [S, d/2]. Returns (q, k, v),
     bf16 [B, S, H, d] (or the given output tensors, any strides with d contiguous)."""
@@ -254,17 +254,11 @@ def sfa_qkv_prologue(x, w_folded, cos, sin, heads: int, head_dim: int, eps: floa
                 t.stride(3) != 1:
             raise ValueError(f"{name} must be bf16 [B, S, H, d] with d contiguous")
         outs.append(t)
-    if workspace is None:
-        n = ctypes.c_size_t()
-        check(lib().sfa_prologue_workspace_bytes(ctypes.byref(g), ctypes.byref(n)),
-              "sfa_prologue_workspace_bytes")
-        workspace = torch.empty(n.value, dtype=torch.uint8, device=x.device)
     xt = Tensor(x.data_ptr(), x.stride(0), x.stride(1), 0)
     ts = [Tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2)) for t in outs]
     check(lib().sfa_qkv_prologue(ctypes.byref(g), xt, ctypes.c_void_p(w_folded.data_ptr()),
                                  ctypes.c_void_p(cos.data_ptr()), ctypes.c_void_p(sin.data_ptr()),
-                                 *ts, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
-                                 _stream_ptr(stream)), "sfa_qkv_prologue")
+                                 *ts, _stream_ptr(stream)), "sfa_qkv_prologue")
     return tuple(outs)
 
 

@@ -234,23 +234,13 @@ int sfa_prologue_fold(const void* w, const void* gamma, void* w_folded, int32_t 
                                     static_cast<hipStream_t>(stream)));
 }
 
-int sfa_prologue_workspace_bytes(const sfa_prologue_geometry* g, size_t* bytes) {
-  if (!bytes) return SFA_ERR_INVALID;
-  const int st = validate_prologue(g);
-  if (st != SFA_OK) return st;
-  *bytes = align256(size_t(g->batch) * g->seq * 4);
-  return SFA_OK;
-}
-
 int sfa_qkv_prologue(const sfa_prologue_geometry* g, sfa_tensor x, const void* w,
                      const float* cosv, const float* sinv, sfa_tensor q, sfa_tensor k, sfa_tensor v,
-                     void* ws, size_t ws_bytes, void* stream) {
+                     void* stream) {
   int st = validate_prologue(g);
   if (st != SFA_OK) return st;
-  if (!w || !cosv || !sinv || !ws || !x.data) return SFA_ERR_INVALID;
-  if (ws_bytes < size_t(g->batch) * g->seq * 4) return SFA_ERR_INVALID;
-  if (!aligned16(w) || !aligned16(cosv) || !aligned16(sinv) || !aligned16(x.data) ||
-      (reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+  if (!w || !cosv || !sinv || !x.data) return SFA_ERR_INVALID;
+  if (!aligned16(w) || !aligned16(cosv) || !aligned16(sinv) || !aligned16(x.data))
     return SFA_ERR_UNSUPPORTED;
   if (x.stride_b < 0 || x.stride_s < g->model_dim) return SFA_ERR_INVALID;
   if ((x.stride_b | x.stride_s) & 7) return SFA_ERR_UNSUPPORTED;
@@ -278,7 +268,6 @@ int sfa_qkv_prologue(const sfa_prologue_geometry* g, sfa_tensor x, const void* w
   p.w = static_cast<const uint16_t*>(w);
   p.cosv = cosv;
   p.sinv = sinv;
-  p.rstd = static_cast<float*>(ws);
   const sfa_tensor* outs[3] = {&q, &k, &v};
   for (int i = 0; i < 3; ++i) {
     p.out[i] = static_cast<uint16_t*>(outs[i]->data);

@@ -170,7 +170,6 @@ struct ProParams {
   const uint16_t* w;      // W' = gamma * W, [3*H*d][C] bf16
   const float* cosv;      // [S][d/2]
   const float* sinv;
-  float* rstd;            // [B][S] workspace
   uint16_t* out[3];       // q, k, v
   int64_t osb[3], oss[3], osh[3];
   int32_t B, S, C, H, d;

@@ -8,8 +8,8 @@
 //
 // RMSNorm folds into the projection: rms(x) * gamma . W = rstd * x . (gamma W),
 // so the weights are pre-multiplied by gamma once (sfa_prologue_fold, bf16) and
-// the kernel scales each token's outputs by its inverse RMS (rstd_kernel, a
-// memory-bound pre-pass). The contraction runs as D[feature][token] =
+// the kernel scales each token's outputs by its inverse RMS, which it sums up
+// from the x operands it already holds. The contraction runs as D[feature][token] =
 // W'[feature][:] . x[token][:] on v_mfma_f32_32x32x16_bf16 with W' as the A
 // operand and x as the B operand, so the accumulator lane holds one token and
 // 16 features; a head's rotation pairs (e, e + d/2) then sit in the same lane
@@ -20,29 +20,6 @@
 namespace {
 
 using sfa::ProParams;
-
-// ---- inverse RMS per token: one wave per row of C elements ----
-__global__ __launch_bounds__(256) void rstd_kernel(ProParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // b * S + s
-  if (row >= int64_t(p.B) * p.S) return;
-  const int b = int(row / p.S), s = int(row - int64_t(b) * p.S);
-  const uint16_t* xr = p.x + b * p.xsb + int64_t(s) * p.xss;
-  float acc = 0.f;
-  for (int c = 8 * lane; c < p.C; c += 512) {
-    const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = __uint_as_float(wv[i] << 16), hi = __uint_as_float(wv[i] & 0xffff0000u);
-      acc = fmaf(lo, lo, acc);
-      acc = fmaf(hi, hi, acc);
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) acc += __shfl_xor(acc, m, 64);
-  if (lane == 0) p.rstd[row] = 1.0f / sqrtf(acc / float(p.C) + p.eps);
-}
 
 // ---- W' = bf16(gamma[c] * W[n][c]) ----
 __global__ __launch_bounds__(256) void fold_kernel(const uint16_t* w, const uint16_t* gamma,
@@ -59,66 +36,80 @@ __global__ __launch_bounds__(256) void fold_kernel(const uint16_t* w, const uint
 }
 
 // ---- the fused projection ----
-// LDS stage (64 KB): A = 256 W' rows x 128 B at [0, 32 KB), B = 256 x rows x
-// 128 B at [32 KB, 64 KB); two stages. Row r keeps its 16-byte chunk c at
-// position c ^ ((r >> 1) & 7), applied through the DMA source address, so the
-// 16 lanes of one operand read hit 16 different bank groups.
+// A workgroup computes a 256-feature x 256-token tile; each wave owns 128
+// features x (512 / WAVES) tokens, so every 16-byte LDS operand read of W'
+// feeds 16 / WAVES MFMAs and every read of x feeds four. LDS stage (64 KB):
+// A = 256 W' rows x 128 B at [0, 32 KB), B = 256 x rows x 128 B at
+// [32 KB, 64 KB); two stages. Row r keeps its 16-byte chunk c at position
+// c ^ ((r >> 1) & 7), applied through the DMA source address, so the 16 lanes
+// of one operand read hit 16 bank groups. The token's sum of squares comes from
+// the same B operand registers (dot2 of each bf16 pair with itself), so the
+// norm needs no pass of its own.
 constexpr int kStageBytes = 65536;
 constexpr int kHalf = 32768;
+
+// Wait for every LDS read of this wave (vmcnt and expcnt left at their maxima).
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 __device__ inline void dma16(const char* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)lds_dst, 16, 0, 0);
 }
 
-template <int D>
-__global__ __launch_bounds__(512, 1) void prologue_kernel(ProParams p) {
+// Workgroup -> (feature tile, token tile). Workgroups go to the 8 XCDs round
+// robin, so XCD x runs workgroups x, x + 8, ...; each XCD takes a contiguous
+// share of a grouped order that walks 6 token tiles x 6 feature tiles at a
+// time, so the ~32 workgroups an XCD runs at once share their W' and x slices
+// through its L2 (12 slices fetched per 36 tiles instead of 2 per tile).
+__device__ inline void tile_of(int bid, int nf, int T, int* ftile, int* ttile) {
+  constexpr int G = 6, FG = 6;
+  const int nblk = nf * T;
+  const int per = nblk / 8, rem = nblk - 8 * (nblk / 8);
+  const int x = bid & 7, i = bid >> 3;
+  const int j = x * per + min(x, rem) + i;
+  const int tg = j / (G * nf);
+  const int gt = min(G, T - tg * G);
+  const int r = j - tg * G * nf;
+  const int fg = r / (gt * FG);
+  const int rr = r - fg * gt * FG;
+  *ttile = tg * G + rr % gt;
+  *ftile = fg * FG + rr / gt;
+}
+
+template <int D, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 1) void prologue_kernel(ProParams p) {
+  constexpr int WPH = WAVES / 2;        // waves per 128-feature half
+  constexpr int TT = 8 / WPH;           // 32-token tiles per wave
+  constexpr int SL = 64 / WAVES;        // 1 KB DMA requests per wave per stage
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wf = wave >> 2, wt = wave & 3;   // 128 features x 64 tokens per wave
+  const int wf = wave / WPH, wt = wave % WPH;
 
-  // workgroup -> (token tile, feature tile); each run of 8 * ntile_f workgroups
-  // gives every XCD the feature tiles of one token tile (its x rows stay in L2)
-  const int nf = p.ntile_f;
-  const int nblk = nf * p.B * p.ntile_t;
-  const int run = 8 * nf;
-  int logical = blockIdx.x;
-  if (int(blockIdx.x) < (nblk / run) * run) {
-    const int c = blockIdx.x / run, r = blockIdx.x - c * run;
-    logical = c * run + (r & 7) * nf + (r >> 3);
-  }
-  const int ttile = logical / nf, ftile = logical - ttile * nf;
+  int ftile, ttile;
+  tile_of(blockIdx.x, p.ntile_f, p.B * p.ntile_t, &ftile, &ttile);
   const int b = ttile / p.ntile_t;
   const int tok0 = (ttile - b * p.ntile_t) * sfa::kProTile;
   const int n0 = ftile * sfa::kProTile;
 
-  // DMA slots of this wave: 8 x 1 KB per stage (slots 0-31 W' rows, 32-63 x rows)
-  const char* srcb[8];
-  uint32_t srco[8];
-  int dsto[8];
-  const char* wbase = reinterpret_cast<const char*>(p.w) + int64_t(n0) * p.C * 2;
-  const char* xbase = reinterpret_cast<const char*>(p.x + b * p.xsb + int64_t(tok0) * p.xss);
+  // DMA: the first half of the waves fetches the 256 W' rows, the second the 256 x rows
+  const bool is_w = wave < WPH;
+  const char* src = is_w ? reinterpret_cast<const char*>(p.w) + int64_t(n0) * p.C * 2
+                         : reinterpret_cast<const char*>(p.x + b * p.xsb + int64_t(tok0) * p.xss);
+  uint32_t srco[SL];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int slot = wave * 8 + j;
-    const int r = (slot & 31) * 8 + (lane >> 3);        // tile row
-    const int c = (lane & 7) ^ ((r >> 1) & 7);          // logical chunk of this lane
-    if (slot < 32) {
-      srcb[j] = wbase;
-      srco[j] = uint32_t(r * p.C * 2 + c * 16);
-      dsto[j] = slot * 1024;
-    } else {
-      const int rr = min(r, p.S - 1 - tok0);             // past the sequence: repeat the last row
-      srcb[j] = xbase;
-      srco[j] = uint32_t(int64_t(rr) * p.xss * 2 + c * 16);
-      dsto[j] = kHalf + (slot - 32) * 1024;
-    }
+  for (int j = 0; j < SL; ++j) {
+    const int r = (wt * SL + j) * 8 + (lane >> 3);                  // tile row
+    const int c = (lane & 7) ^ ((r >> 1) & 7);                      // logical chunk of this lane
+    const int rr = is_w ? r : min(r, p.S - 1 - tok0);               // past S: repeat the last row
+    srco[j] = uint32_t(int64_t(rr) * (is_w ? p.C : p.xss) * 2 + c * 16);
   }
-  auto issue = [&](int buf, int k0) {
+  char* dst0 = lds + (is_w ? 0 : kHalf) + wt * SL * 1024;
+  auto issue = [&](int st) {
+    char* d = dst0 + (st & 1) * kStageBytes;
+    const int koff = st * sfa::kProKStage * 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      dma16(srcb[j] + uint64_t(srco[j]) + k0 * 2, lds + buf * kStageBytes + dsto[j]);
+    for (int j = 0; j < SL; ++j) dma16(src + uint64_t(srco[j]) + koff, d + j * 1024);
   };
 
   // operand read offsets: row bits 1..3 equal those of l32 for every tile
@@ -128,39 +119,92 @@ __global__ __launch_bounds__(512, 1) void prologue_kernel(ProParams p) {
   for (int ks = 0; ks < 4; ++ks) {
     const int x = (((2 * ks + g) ^ sw) * 16);
     aoff[ks] = uint32_t(l32 * 128 + wf * 128 * 128 + x);
-    boff[ks] = uint32_t(kHalf + l32 * 128 + wt * 64 * 128 + x);
+    boff[ks] = uint32_t(kHalf + l32 * 128 + wt * TT * 32 * 128 + x);
   }
+  struct Frags {
+    bf16x8 a[4], b[TT];
+  };
+  auto load = [&](Frags& f, int st, int ks) {
+    const char* sb = lds + (st & 1) * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(sb + aoff[ks] + i * 4096);
+#pragma unroll
+    for (int i = 0; i < TT; ++i) f.b[i] = *reinterpret_cast<const bf16x8*>(sb + boff[ks] + i * 4096);
+  };
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][TT];
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < TT; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[f][t][i] = 0.f;
+  float ss[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) ss[t] = 0.f;
 
-  const int nst = p.C / sfa::kProKStage;
-  issue(0, 0);
-  for (int st = 0; st < nst; ++st) {
-    wait_vm<0>();
-    __syncthreads();
-    if (st + 1 < nst) issue((st + 1) & 1, (st + 1) * sfa::kProKStage);
-    const char* sb = lds + (st & 1) * kStageBytes;
+  auto mma = [&](const Frags& f) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 a[4], bb[2];
+    for (int t = 0; t < TT; ++t) {
+      const auto v = __builtin_bit_cast(uint4, f.b[t]);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-        a[f] = *reinterpret_cast<const bf16x8*>(sb + aoff[ks] + f * 32 * 128);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        bb[t] = *reinterpret_cast<const bf16x8*>(sb + boff[ks] + t * 32 * 128);
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f], bb[t], acc[f][t], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2 h = __builtin_bit_cast(bf16x2, u[i]);
+        ss[t] = __builtin_amdgcn_fdot2_f32_bf16(h, h, ss[t], false);
+      }
+      asm volatile("" : "+v"(ss[t]));   // keep the sums here, beside their operands
     }
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+        acc[fi][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[fi], f.b[t], acc[fi][t], 0, 0, 0);
+  };
+
+  // K loop: stage st is in buffer st & 1; the DMA of stage st + 2 starts once every wave
+  // has read stage st, and the first operands of stage st + 1 load under the last
+  // MFMAs of stage st.
+  const int nst = p.C / sfa::kProKStage;
+  issue(0);
+  if (nst > 1) issue(1);
+  if (nst > 1) wait_vm<SL>(); else wait_vm<0>();
+  __syncthreads();
+  // Each MFMA group runs while the operands of the next one load. The explicit
+  // lgkmcnt(0) before each load batch retires the batch issued one group earlier
+  // (long landed by then), so the compiler sees no LDS read pending when the MFMAs
+  // use it and does not wait for the batch just issued; the sched_barrier fences
+  // keep the scheduler from moving loads next to their first use.
+  Frags fr[2];
+  load(fr[0], 0, 0);
+  auto step = [&](Frags& next, int st, int ks, Frags& cur) {
+    wait_lgkm0();
+    __builtin_amdgcn_sched_barrier(0);
+    load(next, st, ks);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(cur);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int st = 0; st < nst; ++st) {
+    step(fr[1], st, 1, fr[0]);
+    step(fr[0], st, 2, fr[1]);
+    step(fr[1], st, 3, fr[0]);
+    if (st + 1 < nst) {
+      wait_vm<0>();          // stage st + 1 has landed (this wave's part) ...
+      __syncthreads();       // ... everybody's, and everybody has read stage st
+      if (st + 2 < nst) issue(st + 2);
+    }
+    // unconditional (after the last stage it reads a stale buffer and is unused), so
+    // both paths into the next iteration leave the same loads in flight
+    step(fr[0], st + 1, 0, fr[1]);
+  }
+
+  // inverse RMS of the tokens of this lane: the two lane halves hold alternate chunks
+  float rs[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    const float tot = ss[t] + __shfl_xor(ss[t], 32, 64);
+    rs[t] = 1.0f / sqrtf(tot / float(p.C) + p.eps);
   }
 
   // epilogue: row scale, rotation of q and k, bf16 store into [b][s][h][e]
@@ -170,15 +214,14 @@ __global__ __launch_bounds__(512, 1) void prologue_kernel(ProParams p) {
   uint16_t* ob = p.out[which];
   const int64_t osb = p.osb[which], oss = p.oss[which], osh = p.osh[which];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int tok = tok0 + 64 * wt + 32 * t + l32;
+  for (int t = 0; t < TT; ++t) {
+    const int tok = tok0 + wt * TT * 32 + 32 * t + l32;
     const int tc = min(tok, p.S - 1);
-    const float rs = p.rstd[int64_t(b) * p.S + tc];
     float y[4][16];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[f][i] = acc[f][t][i] * rs;
+      for (int i = 0; i < 16; ++i) y[f][i] = acc[f][t][i] * rs[t];
     if (which < 2) {
       // pairs: D = 128: tiles (0, 2), (1, 3); D = 64: tiles (0, 1), (2, 3)
 #pragma unroll
@@ -231,15 +274,15 @@ hipError_t sfa_launch_fold(const uint16_t* w, const uint16_t* gamma, uint16_t* o
 }
 
 hipError_t sfa_launch_prologue(const sfa::ProParams& p, hipStream_t stream) {
-  const int64_t rows = int64_t(p.B) * p.S;
-  hipLaunchKernelGGL(rstd_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  auto kern = p.d == 128 ? prologue_kernel<128> : prologue_kernel<64>;
+  hipError_t e;
+  // 8 waves (two per SIMD, 216 registers): measured as fast as 4 waves of 128 x 128
+  // (which needs all 512 registers and spills in the epilogue)
+  constexpr int waves = 8;
+  auto kern = p.d == 128 ? prologue_kernel<128, waves> : prologue_kernel<64, waves>;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
   if (e != hipSuccess) return e;
   const int blocks = p.ntile_f * p.B * p.ntile_t;
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(512), 2 * kStageBytes, stream, p);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * 64), 2 * kStageBytes, stream, p);
   return hipGetLastError();
 }

@@ -279,21 +279,17 @@ def test_generic_blocks_match_the_oracle_mask(L, F, T, w):
     (dict(heads=128, head_dim=128, model_dim=65536), _lib.SFA_ERR_UNSUPPORTED),  # W' > 2 GiB
 ])
 def test_prologue_geometry_errors(L, kw, status):
+    """Geometry is checked first, before any pointer is looked at (this runs on CPU)."""
     base = dict(batch=1, seq=100, model_dim=256, heads=4, head_dim=64, eps=1e-6)
     base.update(kw)
     g = _lib.PrologueGeometry(base["batch"], base["seq"], base["model_dim"], base["heads"],
                               base["head_dim"], base["eps"])
-    n = ctypes.c_size_t()
-    assert L.sfa_prologue_workspace_bytes(ctypes.byref(g), ctypes.byref(n)) == status
-
-
-def test_prologue_workspace_is_one_float_per_token(L):
-    for B, S in [(1, 100), (2, 50400), (3, 1)]:
-        g = _lib.PrologueGeometry(B, S, 1536, 12, 128, 1e-6)
-        n = ctypes.c_size_t()
-        assert L.sfa_prologue_workspace_bytes(ctypes.byref(g), ctypes.byref(n)) == 0
-        assert n.value >= 4 * B * S and n.value % 256 == 0 and n.value - 4 * B * S < 256
-    assert L.sfa_prologue_workspace_bytes(None, ctypes.byref(n)) == _lib.SFA_ERR_INVALID
+    t = _lib.Tensor(1 << 20, 1 << 16, 256, 0)
+    P = ctypes.c_void_p
+    assert L.sfa_qkv_prologue(ctypes.byref(g), t, P(1 << 22), P(1 << 23), P(1 << 24), t, t, t,
+                              None) == status
+    assert L.sfa_qkv_prologue(None, t, P(1 << 22), P(1 << 23), P(1 << 24), t, t, t, None) == \
+        _lib.SFA_ERR_INVALID
 
 
 def test_prologue_call_validation_happens_before_any_launch(L):
@@ -306,28 +302,24 @@ def test_prologue_call_validation_happens_before_any_launch(L):
     assert fold(P(4096 + 2), P(8192), P(1 << 20), 16, 64, None) == _lib.SFA_ERR_UNSUPPORTED
 
     B, S, C, H, d = 1, 100, 256, 4, 64
-    g = _lib.PrologueGeometry(B, S, C, H, d, 1e-6)
+    g = ctypes.byref(_lib.PrologueGeometry(B, S, C, H, d, 1e-6))
     x = _lib.Tensor(1 << 20, S * C, C, 0)
     w, cs, sn = P(1 << 22), P(1 << 23), P(1 << 24)
     outs = [_lib.Tensor((1 << 26) * (i + 1), S * H * d, H * d, d) for i in range(3)]
-    ws, need = P(1 << 25), 4 * B * S
     Q = L.sfa_qkv_prologue
-    assert Q(None, x, w, cs, sn, *outs, ws, need, None) == _lib.SFA_ERR_INVALID
-    assert Q(ctypes.byref(g), x, None, cs, sn, *outs, ws, need, None) == _lib.SFA_ERR_INVALID
-    assert Q(ctypes.byref(g), x, w, None, sn, *outs, ws, need, None) == _lib.SFA_ERR_INVALID
-    assert Q(ctypes.byref(g), x, w, cs, sn, *outs, None, need, None) == _lib.SFA_ERR_INVALID
-    assert Q(ctypes.byref(g), x, w, cs, sn, *outs, ws, need - 1, None) == _lib.SFA_ERR_INVALID
-    assert Q(ctypes.byref(g), x, w, cs, sn, *outs, P((1 << 25) + 16), need, None) == \
-        _lib.SFA_ERR_UNSUPPORTED
-    assert Q(ctypes.byref(g), x, P((1 << 22) + 8), cs, sn, *outs, ws, need, None) == \
-        _lib.SFA_ERR_UNSUPPORTED
-    assert Q(ctypes.byref(g), _lib.Tensor(1 << 20, S * C, C - 8, 0), w, cs, sn, *outs, ws, need,
-             None) == _lib.SFA_ERR_INVALID                        # rows overlap
-    assert Q(ctypes.byref(g), _lib.Tensor(1 << 20, S * C, C + 4, 0), w, cs, sn, *outs, ws, need,
-             None) == _lib.SFA_ERR_UNSUPPORTED                    # row stride not 16-byte
+    assert Q(g, x, None, cs, sn, *outs, None) == _lib.SFA_ERR_INVALID
+    assert Q(g, x, w, None, sn, *outs, None) == _lib.SFA_ERR_INVALID
+    assert Q(g, x, w, cs, None, *outs, None) == _lib.SFA_ERR_INVALID
+    assert Q(g, _lib.Tensor(None, S * C, C, 0), w, cs, sn, *outs, None) == _lib.SFA_ERR_INVALID
+    assert Q(g, x, P((1 << 22) + 8), cs, sn, *outs, None) == _lib.SFA_ERR_UNSUPPORTED
+    assert Q(g, x, w, P((1 << 23) + 4), sn, *outs, None) == _lib.SFA_ERR_UNSUPPORTED
+    assert Q(g, _lib.Tensor(1 << 20, S * C, C - 8, 0), w, cs, sn, *outs, None) == \
+        _lib.SFA_ERR_INVALID                                      # rows overlap
+    assert Q(g, _lib.Tensor(1 << 20, S * C, C + 4, 0), w, cs, sn, *outs, None) == \
+        _lib.SFA_ERR_UNSUPPORTED                                  # row stride not 16-byte
     bad_out = _lib.Tensor(1 << 26, S * H * d, H * d + 2, d)
-    assert Q(ctypes.byref(g), x, w, cs, sn, bad_out, outs[1], outs[2], ws, need, None) == \
-        _lib.SFA_ERR_UNSUPPORTED
+    assert Q(g, x, w, cs, sn, bad_out, outs[1], outs[2], None) == _lib.SFA_ERR_UNSUPPORTED
+    null_out = _lib.Tensor(None, S * H * d, H * d, d)
+    assert Q(g, x, w, cs, sn, outs[0], null_out, outs[2], None) == _lib.SFA_ERR_INVALID
     on_x = _lib.Tensor((1 << 20) + 64, S * H * d, H * d, d)       # output aliasing x
-    assert Q(ctypes.byref(g), x, w, cs, sn, outs[0], on_x, outs[2], ws, need, None) == \
-        _lib.SFA_ERR_INVALID
+    assert Q(g, x, w, cs, sn, outs[0], on_x, outs[2], None) == _lib.SFA_ERR_INVALID
