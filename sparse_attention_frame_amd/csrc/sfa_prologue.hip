@@ -207,12 +207,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prologue_kernel(ProParams p) {
     rs[t] = 1.0f / sqrtf(tot / float(p.C) + p.eps);
   }
 
-  // epilogue: row scale, rotation of q and k, bf16 store into [b][s][h][e]
+  // epilogue: row scale, rotation of q and k, bf16 store into [b][s][h][e] through LDS
   const int HD = p.H * D;
   const int which = n0 / HD;                  // 0 q, 1 k, 2 v (tiles never straddle)
   const int nw = n0 + 128 * wf - which * HD;  // first feature of this wave inside its tensor
   uint16_t* ob = p.out[which];
   const int64_t osb = p.osb[which], oss = p.oss[which], osh = p.osh[which];
+  // the stage buffers are free once every wave has passed this barrier; each wave then
+  // stages its TT * 32 tokens x 256 B there, so the global stores are whole rows
+  __syncthreads();
+  char* stg = lds + wave * (TT * 32 * 256);
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
     const int tok = tok0 + wt * TT * 32 + 32 * t + l32;
@@ -244,20 +248,30 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prologue_kernel(ProParams p) {
         }
       }
     }
-    if (tok < p.S) {
-      uint16_t* orow = ob + b * osb + int64_t(tok) * oss;
+    // bf16 into this wave's staging rows: [token][128 features] (256 B per token), the
+    // 16-byte chunk index XOR-swizzled by token % 16
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int feat = nw + 32 * f;             // first feature of tile f
-        const int h = feat / D, e0 = feat - h * D;
+    for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          uint2 w2;
-          w2.x = pack_bf16x2(y[f][4 * qd], y[f][4 * qd + 1]);
-          w2.y = pack_bf16x2(y[f][4 * qd + 2], y[f][4 * qd + 3]);
-          *reinterpret_cast<uint2*>(orow + h * osh + e0 + 8 * qd + 4 * g) = w2;
-        }
+      for (int qd = 0; qd < 4; ++qd) {
+        const int r = 32 * t + l32;
+        uint2 w2;
+        w2.x = pack_bf16x2(y[f][4 * qd], y[f][4 * qd + 1]);
+        w2.y = pack_bf16x2(y[f][4 * qd + 2], y[f][4 * qd + 3]);
+        *reinterpret_cast<uint2*>(stg + r * 256 + (((4 * f + qd) ^ (r & 15)) * 16) + 8 * g) = w2;
       }
+  }
+  // write back whole rows: 16 lanes cover one token's 256 contiguous bytes (one head of
+  // 128, or two of 64), 4 tokens per instruction
+#pragma unroll
+  for (int i = 0; i < TT * 8; ++i) {
+    const int r = 4 * i + (lane >> 4), c = lane & 15;
+    const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 256 + ((c ^ (r & 15)) * 16));
+    const int tok = tok0 + wt * TT * 32 + r;
+    if (tok < p.S) {
+      const int feat = nw + 8 * c;
+      const int h = feat / D, e = feat - h * D;
+      *reinterpret_cast<uint4*>(ob + b * osb + int64_t(tok) * oss + h * osh + e) = v;
     }
   }
 }
