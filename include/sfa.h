@@ -219,7 +219,8 @@ int sfa_prologue_fold(const void* w, const void* gamma, void* w_folded, int32_t 
 /* x: bf16 [B][S][C] (stride_b, stride_s in elements, C contiguous, stride_s <= 2^22;
  * stride_h ignored). w_folded: bf16 [3*H*d][C] from sfa_prologue_fold. cos, sin:
  * fp32 [S][d/2]. q, k, v: bf16 [B][S][H][d] in any sfa_tensor strides (they must
- * not overlap x). One launch on `stream`. Returns SFA_ERR_INVALID for null or
+ * not overlap x, and share no element with each other; interleaved views of one
+ * [B][S][3][H][d] buffer are fine). Fewer than 2^31 tiles of 256 x 256. One launch on `stream`. Returns SFA_ERR_INVALID for null or
  * overlapping arguments, SFA_ERR_UNSUPPORTED for shapes, strides or alignments
  * outside the rules above (data pointers 16-byte aligned, strides multiples of 8). */
 int sfa_qkv_prologue(const sfa_prologue_geometry* geom, sfa_tensor x, const void* w_folded,

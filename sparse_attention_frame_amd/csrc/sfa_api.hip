@@ -216,6 +216,9 @@ int validate_prologue(const sfa_prologue_geometry* g) {
   // 32-bit offsets: W' rows of one tile, tokens, feature and tile counts
   if (N * g->model_dim * 2 > (int64_t(1) << 31) - 1) return SFA_ERR_UNSUPPORTED;
   if (int64_t(g->batch) * g->seq > (int64_t(1) << 30)) return SFA_ERR_UNSUPPORTED;
+  // one workgroup per 256 x 256 tile, indexed with 32-bit arithmetic
+  const int64_t tiles = N / kProTile * g->batch * ((int64_t(g->seq) + kProTile - 1) / kProTile);
+  if (tiles > (int64_t(1) << 31) - 1) return SFA_ERR_UNSUPPORTED;
   return SFA_OK;
 }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }

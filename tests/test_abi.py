@@ -277,6 +277,8 @@ def test_generic_blocks_match_the_oracle_mask(L, F, T, w):
     (dict(seq=0), _lib.SFA_ERR_INVALID),
     (dict(heads=0), _lib.SFA_ERR_INVALID),
     (dict(heads=128, head_dim=128, model_dim=65536), _lib.SFA_ERR_UNSUPPORTED),  # W' > 2 GiB
+    (dict(batch=4096, seq=262144, heads=512, head_dim=128, model_dim=64),
+     _lib.SFA_ERR_UNSUPPORTED),                                   # >= 2^31 workgroup tiles
 ])
 def test_prologue_geometry_errors(L, kw, status):
     """Geometry is checked first, before any pointer is looked at (this runs on CPU)."""
