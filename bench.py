@@ -54,8 +54,20 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, q_np, k_np, v_np, budget_s=12.0):
-    """Time the oracle (as it stands) on whole query frames of head 0 until ~budget_s."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
+def cpu_baseline(wl, q_np, k_np, v_np, out_head0=None, budget_s=12.0):
+    """Time the oracle (as it stands) on whole query frames of head 0 until ~budget_s. With
+    the GPU output of head 0 ([S, d] float32) it also reports the parity of those rows."""
     import numpy as np
 
     import oracle
@@ -69,39 +81,66 @@ def cpu_baseline(wl, q_np, k_np, v_np, budget_s=12.0):
     order = [F // 2] + [f for f in range(F + 1) if f != F // 2]   # a full-window frame first
     flops = 0.0
     done = []
+    refs = []
     t0 = time.perf_counter()
     for f in order:
         rows = np.arange(f * T, (f + 1) * T)
-        oracle.attention_rows(q_np, k_np, v_np, F, T, wl.window, 0, 0, rows)
+        refs.append((rows, oracle.attention_rows(q_np, k_np, v_np, F, T, wl.window, 0, 0, rows)))
         nkeys = len(oracle.key_frames(f, F, wl.window)) * T
         flops += 4.0 * d * T * nkeys
         done.append(f)
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"head 0, query frames {done} ({len(done) * T} rows) of the 720p layer, "
-                      f"fp64 dense-masked numpy, {dt:.1f} s"}
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+           "kind": "oracle", "cpu": cpu_model(),
+           "sample": f"head 0, query frames {done} ({len(done) * T} rows) of the {wl.name} layer, "
+                     f"fp64 dense-masked numpy, {dt:.1f} s"}
+    if out_head0 is not None:
+        # parity of the same rows in the same run (tolerance: max-abs 2e-2, rel-L2 5e-3)
+        got = np.concatenate([out_head0[r] for r, _ in refs]).astype(np.float64)
+        ref = np.concatenate([o for _, o in refs])
+        diff = got - ref
+        res["parity"] = {"rows": int(len(ref)), "max_abs": float(np.abs(diff).max()),
+                         "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(ref)),
+                         "pass": bool(np.abs(diff).max() <= 2e-2
+                                      and np.linalg.norm(diff) <= 5e-3 * np.linalg.norm(ref))}
+    return res
 
 
-def cpu_baseline_prologue(pw, x, gamma, w, cos, sin, budget_s=12.0):
-    """Time the oracle prologue on chunks of 512 tokens until ~budget_s; TFLOP/s."""
+def cpu_baseline_prologue(pw, x, gamma, w, cos, sin, outs=None, budget_s=12.0):
+    """Time the oracle prologue on chunks of 512 tokens until ~budget_s; TFLOP/s. With the
+    GPU's q, k, v it also reports the parity of the chunks done (tolerance of the tests:
+    |got - ref| <= 1.2e-2 + 4e-3 |ref| element by element, rel-L2 <= 5e-3)."""
     import numpy as np
 
     import oracle
 
     flops_tok = 2.0 * pw.model_dim * 3 * pw.heads * pw.head_dim
     done, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and done < pw.seq:
+    worst, d2, r2 = -np.inf, 0.0, 0.0
+    timed = 0.0
+    while timed < budget_s and done < pw.seq:
         sl = slice(done, min(done + 512, pw.seq))
-        oracle.qkv_prologue(x[:, sl], gamma, w, cos[sl], sin[sl], pw.heads, pw.head_dim)
+        t1 = time.perf_counter()
+        refs = oracle.qkv_prologue(x[:, sl], gamma, w, cos[sl], sin[sl], pw.heads, pw.head_dim)
+        timed += time.perf_counter() - t1
+        if outs is not None:
+            for got_t, ref in zip(outs, refs):
+                got = got_t[:, sl].float().cpu().numpy().astype(np.float64)
+                diff = np.abs(got - ref)
+                worst = max(worst, float((diff - (1.2e-2 + 4e-3 * np.abs(ref))).max()))
+                d2 += float((diff ** 2).sum())
+                r2 += float((ref ** 2).sum())
         done = sl.stop
-    el = time.perf_counter() - t0
-    return {"value": round(done * pw.batch * flops_tok / el / 1e12, 6), "unit": "TFLOP/s",
-            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
-            "kind": "oracle",
-            "sample": f"first {done} tokens of batch 0 in 512-token chunks, fp64, {el:.1f} s"}
+    res = {"value": round(done * pw.batch * flops_tok / timed / 1e12, 6), "unit": "TFLOP/s",
+           "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+           "kind": "oracle", "cpu": cpu_model(),
+           "sample": f"first {done} tokens of batch 0 in 512-token chunks, fp64, {timed:.1f} s"}
+    if outs is not None:
+        rl = (d2 / r2) ** 0.5
+        res["parity"] = {"tokens": done, "rel_l2": rl, "pass": bool(worst <= 0 and rl <= 5e-3)}
+    return res
 
 
 def bench_prologue(args):
@@ -191,7 +230,8 @@ def bench_prologue(args):
     }
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline_prologue(pw, x_np, g_np, w_np, cos_np, sin_np)
+        res["cpu_baseline"] = cpu_baseline_prologue(pw, x_np, g_np, w_np, cos_np, sin_np,
+                                                    outs=(q, k, v))
     print(json.dumps(res), flush=True)
 
 
@@ -293,8 +333,10 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     norms_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    fwd_min = float(np.min([e[1].elapsed_time(e[2]) for e in ev]))
+    fwd_all = [e[1].elapsed_time(e[2]) for e in ev]
+    step_all = [e[0].elapsed_time(e[2]) for e in ev]
+    fwd_ms = float(np.mean(fwd_all))
+    fwd_min = float(np.min(fwd_all))
 
     info = plan.info
     flops = info["active_flops"]
@@ -336,6 +378,9 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_ms, 4),
         "fwd_min_ms": round(fwd_min, 4),
+        "fwd_median_ms": round(float(np.median(fwd_all)), 4),
+        "step_event_median_ms": round(float(np.median(step_all)), 4),
+        "step_event_min_ms": round(float(np.min(step_all)), 4),
         "norms_ms": round(norms_ms, 4),
         "roofline": {"bound": "mfma",
                      "kernel": ("whole step (generic two-pass ablation)" if args.ablation != "none"
@@ -354,7 +399,8 @@ def main():
         res["copy_probe_mib"] = args.copy_probe_mib
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(wl, q_np, k_np, v_np)
+        res["cpu_baseline"] = cpu_baseline(wl, q_np, k_np, v_np,
+                                           out[0, :, 0].float().cpu().numpy())
     print(json.dumps(res), flush=True)
 
 
