@@ -247,6 +247,8 @@ def main():
     ap.add_argument("--lds-stages", type=int, default=0, help="override K/V stages in flight")
     ap.add_argument("--bound-mode", type=int, default=0,
                     help="0: per-head bound (default); 1: per-visible-frame bound")
+    ap.add_argument("--bound-limit", type=float, default=40.0,
+                    help="eligibility threshold of the fixed maximum (negative: every head online)")
     ap.add_argument("--head-groups", type=int, default=1,
                     help="split the heads into this many groups (sfa_attention_groups)")
     ap.add_argument("--group-streams", type=int, default=0,
@@ -280,7 +282,8 @@ def main():
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q_np, k_np, v_np))
     plan = sfa.Plan.for_workload(wl, waves=args.waves, block_q=args.block_q,
-                                 lds_stages=args.lds_stages, bound_mode=args.bound_mode)
+                                 lds_stages=args.lds_stages, bound_mode=args.bound_mode,
+                                 bound_limit=args.bound_limit)
     ws = plan.workspace(dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
@@ -291,7 +294,8 @@ def main():
     if G > 1:
         gplan = sfa.Plan(wl.batch, wl.heads // G, wl.head_dim, wl.frames, wl.tokens_per_frame,
                          wl.window, waves=args.waves, block_q=args.block_q,
-                         lds_stages=args.lds_stages, bound_mode=args.bound_mode)
+                         lds_stages=args.lds_stages, bound_mode=args.bound_mode,
+                         bound_limit=args.bound_limit)
         gws = torch.empty(G * gplan.info["workspace_bytes"], dtype=torch.uint8, device=dev)
         gstreams = [torch.cuda.Stream() for _ in range(args.group_streams)]
 
@@ -370,7 +374,7 @@ def main():
                    "items": info["items"],
                    "active_gflop": round(flops / 1e9, 1),
                    "eligible_heads": int(st["eligible"].sum()), "heads": wl.heads,
-                   "bound_mode": args.bound_mode,
+                   "bound_mode": args.bound_mode, "bound_limit": args.bound_limit,
                    "eligible_query_frames": int(fst["eligible"].sum()),
                    "query_frames": int(fst["eligible"].size),
                    "head_groups": G, "group_streams": args.group_streams,
@@ -388,6 +392,8 @@ def main():
                      "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": (traffic if G == 1 and args.bound_mode == 0
+                                 and wl.name == "720p" and args.bound_limit == 40.0
+                                 and not (args.waves or args.block_q or args.lds_stages)
                                  and args.ablation == "none" else None)},
     }
     if args.copy_probe_mib:

@@ -69,6 +69,13 @@ constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr int kStageKeys = 64;  // keys per LDS stage (4 granules, 2 tiles of 32)
 
+// Online softmax keeps a stale running maximum until a tile's maximum exceeds it by
+// more than kLazy (log2 units). P then stays below 2^kLazy, which bf16 and the fp32
+// sums hold with unchanged relative precision: with fewer than 2^24 keys per row,
+// l < 2^88 and |O| < 2^88 * max|v|, far below 2^127 for any bf16 v up to 2^38. A large
+// kLazy makes rescales rare when the scores are wide.
+constexpr float kLazy = 64.0f;
+
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v;
   v[0] = (__bf16)lo;
@@ -257,9 +264,9 @@ struct Attn {
 #pragma unroll
         for (int i = 1; i < NV; ++i) mx = fmaxf(mx, s[t][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cexp;
-        // lazy rescale: keep the stale maximum while the tile stays within 2^8 of
-        // it (exact up to rounding: numerator and denominator share the shift)
-        const bool grow = mx > mrow[t] + 8.0f;
+        // lazy rescale: keep the stale maximum while the tile stays within 2^kLazy
+        // of it (exact up to rounding: numerator and denominator share the shift)
+        const bool grow = mx > mrow[t] + kLazy;
         if (__ballot(grow) != 0) {
           const float mnew = fmaxf(mrow[t], mx);
           const float alpha = __builtin_amdgcn_exp2f(mrow[t] - mnew);

@@ -60,7 +60,9 @@ struct Item {
 // key stream; groups are sorted by decreasing cost (frame_order). Workgroups
 // are handed to the 8 XCDs round-robin, so inside every run of 8 groups the
 // index is permuted to give each XCD one whole group (shared K/V in its L2)
-// while the launch order still follows decreasing cost.
+// while the launch order still follows decreasing cost. The XCD -> group
+// assignment rotates by one from run to run, so a head whose items are slower
+// (online softmax) does not always land on the same XCD.
 __host__ __device__ inline Item decode_item(int idx, const uint16_t* frame_order, int B, int H,
                                             int nqb, int items) {
   const int run = 8 * nqb;
@@ -69,7 +71,7 @@ __host__ __device__ inline Item decode_item(int idx, const uint16_t* frame_order
   if (idx < full) {
     const int c = idx / run;
     const int r = idx - c * run;
-    logical = c * run + (r & 7) * nqb + (r >> 3);
+    logical = c * run + (((r & 7) + c) & 7) * nqb + (r >> 3);
   }
   const int g = logical / nqb;
   const int qb = logical - g * nqb;
