@@ -126,6 +126,7 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   p->ws.pkmax = take(ngran * bh * 4);          // [b][h][granule], squared norms
   p->ws.pqmax = take(ngran * bh * 4);
   p->ws.vt = take(bh * size_t(D) * size_t(p->S) * 2);  // bf16 V^T [b][h][d][S]
+  p->ws.queue = take(kQueueWords * 4);
   p->ws.total = off;
   *out = p;
   return SFA_OK;
@@ -179,6 +180,7 @@ NormParams norm_params(const sfa_plan* p, const sfa_tensor& q, const sfa_tensor&
   n.psum = reinterpret_cast<float*>(base + p->ws.psum);
   n.pkmax = reinterpret_cast<float*>(base + p->ws.pkmax);
   n.pqmax = reinterpret_cast<float*>(base + p->ws.pqmax);
+  n.queue = reinterpret_cast<int32_t*>(base + p->ws.queue);
   n.B = p->g.batch; n.H = p->g.heads; n.S = p->S; n.D = p->g.head_dim;
   n.nchunk = p->nchunk;
   n.T = p->g.tokens_per_frame; n.F = p->g.frames; n.w = p->g.window;
@@ -526,6 +528,7 @@ int sfa_fwd(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_ten
   f.F = p->g.frames; f.w = p->g.window;
   f.gq = p->gq; f.nqb = p->nqb; f.items = p->items;
   f.c = p->scale * 1.4426950408889634f;
+  f.queue = reinterpret_cast<int32_t*>(base + p->ws.queue);
   memcpy(f.frame_order, p->frame_order, sizeof(f.frame_order));
   return hip_status(
       sfa_launch_fwd(f, p->g.head_dim, p->waves, p->stages, static_cast<hipStream_t>(stream)));

@@ -88,8 +88,12 @@ __host__ __device__ inline Item decode_item(int idx, const uint16_t* frame_order
 
 struct Workspace {
   size_t mu, kmax, qmax, bound, elig, kvis, fbound, felig, qn, qmu, psum, pkmax, pqmax, vt,
-      total;
+      queue, total;
 };
+
+// Work queue of the attention kernel in the workspace: one counter per XCD, a
+// count of workgroups that found no work left, padding to 64 bytes.
+constexpr int kQueueWords = 16;
 
 struct FwdParams {
   const uint16_t* q;
@@ -107,6 +111,7 @@ struct FwdParams {
   int32_t nqb;    // items per (frame, batch, head)
   int32_t items;
   float c;        // scale * log2(e)
+  int32_t* queue; // kQueueWords counters, zero between launches
   uint16_t frame_order[kMaxFrameSlots];
 };
 
@@ -129,6 +134,7 @@ struct NormParams {
   float* psum;
   float* pkmax;   // [b][h][granule]: max ||k - mu||^2 over the 16 tokens of a granule
   float* pqmax;   // [b][h][granule]: max ||q||^2
+  int32_t* queue; // the attention kernel's work queue, zeroed here
   int32_t B, H, S, D, nchunk;
   int32_t T, F, w;
   int32_t bound_mode;

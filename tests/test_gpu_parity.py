@@ -215,6 +215,31 @@ def test_double_run_is_bitwise_identical(sfa):
         np.testing.assert_array_equal(x, y)
 
 
+@pytest.mark.parametrize("name", ["small", "720p"])
+def test_work_queue_covers_every_item_on_repeated_launches(sfa, name):
+    """The attention kernel runs persistent workgroups that take items from per-XCD
+    counters in the workspace (zeroed by sfa_norms, reset by the last workgroup of each
+    launch). A workspace full of garbage, then three launches after one sfa_norms, each
+    into an output full of NaN: every element is written, identically each time."""
+    wl = W.ALL[name]
+    say(f"[work queue] {name}")
+    q, k, v = to_dev(*W.make_inputs_np(wl))
+    plan = sfa.Plan(*geom(wl))
+    ws = plan.workspace()
+    ws.fill_(0xFF)
+    sfa.norms(plan, q, k, v, workspace=ws)
+    first = None
+    for _ in range(3):
+        out = torch.full_like(q, float("nan"))
+        sfa.fwd(plan, q, k, v, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all()
+        if first is None:
+            first = out
+        else:
+            assert torch.equal(out, first)
+
+
 def test_head_subset_and_layouts_are_bitwise_equal(sfa):
     """Head groups see exactly the same mask; strided layouts change nothing."""
     wl = W.SMALL
