@@ -567,7 +567,7 @@ int sfa_attention_groups(const sfa_plan* p, int32_t groups, sfa_tensor q, sfa_te
     for (int i = 0; e == hipSuccess && i < ns; ++i)
       e = hipStreamWaitEvent(static_cast<hipStream_t>(group_streams[i]), fork, 0);
     if (e != hipSuccess) {
-      if (fork) hipEventDestroy(fork);
+      if (fork) (void)hipEventDestroy(fork);  // already failing: report the first error
       return hip_status(e);
     }
   }
@@ -587,8 +587,11 @@ int sfa_attention_groups(const sfa_plan* p, int32_t groups, sfa_tensor q, sfa_te
       e = hipEventRecord(joins[made], static_cast<hipStream_t>(group_streams[made]));
       if (e == hipSuccess) e = hipStreamWaitEvent(main, joins[made], 0);
     }
-    for (int i = 0; i < made; ++i) hipEventDestroy(joins[i]);
-    hipEventDestroy(fork);
+    // destroying a recorded event is legal; its resources go once the work completes
+    for (int i = 0; i <= made; ++i) {
+      const hipError_t d = hipEventDestroy(i < made ? joins[i] : fork);
+      if (d != hipSuccess && e == hipSuccess) e = d;
+    }
     if (st == SFA_OK && e != hipSuccess) st = hip_status(e);
   }
   return st;
