@@ -141,7 +141,10 @@ int sfa_norms(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, vo
  * heads and the online softmax for the others. Reads q and k from their
  * tensors and V^T from the workspace, so sfa_norms must have run on the same
  * q, k, v and workspace earlier on the stream; v itself is only validated. o
- * may not alias q, k or v. */
+ * may not alias q, k or v. The launch is persistent (at most one workgroup per
+ * CU) and takes its work items from counters in the workspace, which sfa_norms
+ * zeroes and every launch leaves at zero: sfa_fwd may run any number of times
+ * after one sfa_norms, but two calls in flight at once on one workspace race. */
 int sfa_fwd(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_tensor o,
             void* workspace, size_t workspace_bytes, void* stream);
 
