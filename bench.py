@@ -26,26 +26,30 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_720p_traffic.json")
 KERNEL_SOURCES = ("sparse_attention_frame_amd/csrc/sfa_attn.h",
                   "sparse_attention_frame_amd/csrc/sfa_fwd.hip",
                   "sparse_attention_frame_amd/csrc/sfa_internal.h")
+PRO_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prologue_kernel_720p_traffic.json")
+PRO_SOURCES = ("sparse_attention_frame_amd/csrc/sfa_attn.h",
+               "sparse_attention_frame_amd/csrc/sfa_prologue.hip",
+               "sparse_attention_frame_amd/csrc/sfa_internal.h")
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     import hashlib
 
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per attention-kernel launch from the committed rocprofv3 counters,
-    or None when the kernel source changed since they were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
+    """HBM bytes per kernel launch from the committed rocprofv3 counters, or None when
+    the kernel source changed since they were taken."""
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256") != kernel_source_hash():
+    if t.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     return t.get("bytes_per_launch")
 
@@ -226,8 +230,15 @@ def bench_prologue(args):
                      "achieved": round(flops / (kern_ms * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(PRO_TRAFFIC_FILE, PRO_SOURCES)},
     }
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 2
+        cx = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        cy = torch.empty_like(cx)
+        torch.neg(cx, out=cy)        # reads and writes exactly copy_probe_mib MiB
+        torch.cuda.synchronize()
+        res["copy_probe_mib"] = args.copy_probe_mib
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline_prologue(pw, x_np, g_np, w_np, cos_np, sin_np,
