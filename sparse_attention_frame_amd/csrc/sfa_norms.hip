@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void final_kernel(NormParams p) {
   q2s[threadIdx.x] = q2;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) {
+    if (int(threadIdx.x) < w) {
       k2s[threadIdx.x] = fmaxf(k2s[threadIdx.x], k2s[threadIdx.x + w]);
       q2s[threadIdx.x] = fmaxf(q2s[threadIdx.x], q2s[threadIdx.x + w]);
     }
