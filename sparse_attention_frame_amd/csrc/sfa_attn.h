@@ -21,11 +21,12 @@
 //   * section "Proving pixels unchanged": P is rounded to bf16 and PV runs on
 //     the bf16 matrix cores with fp32 accumulation.
 //
-// Work decomposition: one workgroup = one work item = one query block of
-// 16*gq rows (gq | T/16) of one (batch, head, frame). WAVES waves each own QT
-// 32-row query tiles; when gq is odd the last tile holds 16 real rows and 16
-// repeats that are computed but never stored. All waves stream the same key
-// granules through LDS.
+// Work decomposition: a work item is one query block of 16*gq rows (gq | T/16)
+// of one (batch, head, frame); a workgroup runs one item at a time (the attention
+// kernel keeps its workgroups resident and hands them items from a queue). WAVES
+// waves each own QT 32-row query tiles; when gq is odd the last tile holds 16 real
+// rows and 16 repeats that are computed but never stored. All waves stream the same
+// key granules through LDS.
 //
 // MFMA orientation (v_mfma_f32_32x32x16_bf16, wave64; 32x32x16 runs at twice
 // the rate of 16x16x32 on this chip):
@@ -43,8 +44,8 @@
 // Staging: the memory-bound prologue (sfa_norms) writes V^T [b][h][d][S] into
 // the workspace (LDS transpose reads run at well under half the rate of plain
 // 16-byte reads on gfx950). K rows and V^T granules then go from HBM straight into LDS by
-// DMA (global_load_lds_dwordx4: no registers, no VALU), double-buffered per
-// 64-key stage. 16-byte chunks are XOR-swizzled through the DMA source address
+// DMA (global_load_lds_dwordx4: no registers, no VALU), in NBUF rotating 64-key
+// stages. 16-byte chunks are XOR-swizzled through the DMA source address
 // so the operand reads are free of bank conflicts:
 //   K   [key][d]            : chunk ^= key % 16 (16 lanes read 16 rows);
 //   V^T [granule][d][16 keys]: half ^= (d / 8) % 2 (16 lanes read 16 rows of 32 B).

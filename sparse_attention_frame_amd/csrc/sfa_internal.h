@@ -56,11 +56,12 @@ struct Item {
   int32_t b, h, f, qb;
 };
 
-// blockIdx -> work item. Groups of `nqb` items share one (frame, batch, head)
-// key stream; groups are sorted by decreasing cost (frame_order). Workgroups
-// are handed to the 8 XCDs round-robin, so inside every run of 8 groups the
+// Item index -> work item. Groups of `nqb` items share one (frame, batch, head)
+// key stream; groups are sorted by decreasing cost (frame_order). Item index i
+// belongs to XCD i % 8 (the attention kernel's queues follow the round-robin
+// order in which workgroups reach the XCDs), so inside every run of 8 groups the
 // index is permuted to give each XCD one whole group (shared K/V in its L2)
-// while the launch order still follows decreasing cost. The XCD -> group
+// while the order still follows decreasing cost. The XCD -> group
 // assignment rotates by one from run to run, so a head whose items are slower
 // (online softmax) does not always land on the same XCD.
 __host__ __device__ inline Item decode_item(int idx, const uint16_t* frame_order, int B, int H,
