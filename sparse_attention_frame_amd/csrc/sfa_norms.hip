@@ -54,17 +54,23 @@ __global__ __launch_bounds__(kThreads) void ksum_kernel(NormParams p) {
   const int cpr = p.D / 8;           // column groups per head
   const int groups = p.H * cpr;
   const int s0 = chunk * kNormChunk;
-  const int s1 = min(p.S, s0 + kNormChunk);
-  for (int cg = threadIdx.x; cg < groups; cg += kThreads) {
+  const int s1 = min(p.S, s0 + kNormChunk);  // s1 - s0 is a multiple of 16
+  for (int cg = threadIdx.x; cg < groups; cg += blockDim.x) {
     const int h = cg / cpr;
     const int e0 = (cg - h * cpr) * 8;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const uint16_t* kp = p.k + b * p.ksb + h * p.ksh + e0;
-    for (int s = s0; s < s1; ++s) {
-      float x[8];
-      unpack8(load16(kp + int64_t(s) * p.kss), x);
+    for (int s = s0; s < s1; s += 4) {
+      uint4 raw[4];  // four rows in flight per lane
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += x[i];
+      for (int t = 0; t < 4; ++t) raw[t] = load16(kp + int64_t(s + t) * p.kss);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float x[8];
+        unpack8(raw[t], x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += x[i];
+      }
     }
     float* out = p.psum + ((int64_t(chunk) * p.B + b) * p.H + h) * p.D + e0;
 #pragma unroll
@@ -109,9 +115,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(NormParams p) {
   const int groups = p.H * CPR;
   const int s0 = chunk * kNormChunk;
   const int s1 = min(p.S, s0 + kNormChunk);
-  // groups is a multiple of CPR and the loop stride 256 is too, so the CPR lanes
-  // of one head always iterate together (shuffles stay inside the group)
-  for (int cgb = 0; cgb < groups; cgb += kThreads) {
+  // groups is a multiple of CPR and the loop stride (a multiple of 64) is too, so
+  // the CPR lanes of one head always iterate together (shuffles stay inside the group)
+  for (int cgb = 0; cgb < groups; cgb += blockDim.x) {
     const int cg = cgb + threadIdx.x;
     const bool active = cg < groups;
     const int h = active ? cg / CPR : 0;
@@ -123,39 +129,44 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(NormParams p) {
     const uint16_t* kp = p.k + b * p.ksb + h * p.ksh + e0;
     const uint16_t* qp = p.q + b * p.qsb + h * p.qsh + e0;
     float kmax2 = 0.f, qmax2 = 0.f;
-    for (int s = s0; s < s1; ++s) {
-      float kx[8], qx[8];
-      if (active) {
-        unpack8(load16(kp + int64_t(s) * p.kss), kx);
-        unpack8(load16(qp + int64_t(s) * p.qss), qx);
-      } else {
+    for (int sb = s0; sb < s1; sb += 4) {  // s1 - s0 is a multiple of 16
+      uint4 kr[4], qr[4];  // four rows of k and q in flight per lane
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kx[i] = qx[i] = 0.f;
+      for (int t = 0; t < 4; ++t) {
+        kr[t] = active ? load16(kp + int64_t(sb + t) * p.kss) : make_uint4(0, 0, 0, 0);
+        qr[t] = active ? load16(qp + int64_t(sb + t) * p.qss) : make_uint4(0, 0, 0, 0);
       }
-      float kc = 0.f, qq = 0.f, qm = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float t = kx[i] - mu[i];
-        kc = fmaf(t, t, kc);
-        qq = fmaf(qx[i], qx[i], qq);
-        qm = fmaf(qx[i], mu[i], qm);
-      }
-      kc = group_sum<CPR>(kc);
-      qq = group_sum<CPR>(qq);
-      qm = group_sum<CPR>(qm);
-      kmax2 = fmaxf(kmax2, kc);
-      qmax2 = fmaxf(qmax2, qq);
-      if (active && (cg % CPR) == 0) {
-        const int64_t row = (int64_t(b) * p.H + h) * p.S + s;
-        p.qn[row] = sqrtf(qq);
-        p.qmu[row] = qm;
-        if ((s & 15) == 15) {  // last token of a granule (S and s0 are multiples of 16)
-          const int64_t at = (int64_t(b) * p.H + h) * (p.S >> 4) + (s >> 4);
-          p.pkmax[at] = kmax2;
-          p.pqmax[at] = qmax2;
+      for (int t = 0; t < 4; ++t) {
+        const int s = sb + t;
+        float kx[8], qx[8];
+        unpack8(kr[t], kx);
+        unpack8(qr[t], qx);
+        float kc = 0.f, qq = 0.f, qm = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float dk = kx[i] - mu[i];
+          kc = fmaf(dk, dk, kc);
+          qq = fmaf(qx[i], qx[i], qq);
+          qm = fmaf(qx[i], mu[i], qm);
         }
+        kc = group_sum<CPR>(kc);
+        qq = group_sum<CPR>(qq);
+        qm = group_sum<CPR>(qm);
+        kmax2 = fmaxf(kmax2, kc);
+        qmax2 = fmaxf(qmax2, qq);
+        if (active && (cg % CPR) == 0) {
+          const int64_t row = (int64_t(b) * p.H + h) * p.S + s;
+          p.qn[row] = sqrtf(qq);
+          p.qmu[row] = qm;
+          if ((s & 15) == 15) {  // last token of a granule (S and s0 are multiples of 16)
+            const int64_t at = (int64_t(b) * p.H + h) * (p.S >> 4) + (s >> 4);
+            p.pkmax[at] = kmax2;
+            p.pqmax[at] = qmax2;
+          }
+        }
+        if ((s & 15) == 15) kmax2 = qmax2 = 0.f;
       }
-      if ((s & 15) == 15) kmax2 = qmax2 = 0.f;
     }
   }
 }
@@ -276,16 +287,20 @@ __global__ __launch_bounds__(256) void vt_kernel(NormParams p) {
 
 hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream) {
   const dim3 grid(p.nchunk, p.B);
-  hipLaunchKernelGGL(ksum_kernel, grid, dim3(kThreads), 0, stream, p);
+  // one lane per (head, 8 columns), rounded up to whole waves (no idle lanes at
+  // H * d / 8 = 192, the 12-head layers), at most kThreads
+  const int groups = p.H * (p.D / 8);
+  const dim3 block(groups < kThreads ? (groups + 63) / 64 * 64 : kThreads);
+  hipLaunchKernelGGL(ksum_kernel, grid, block, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kmean_kernel, dim3(p.B * p.H), dim3(kReduceThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.D == 128)
-    hipLaunchKernelGGL(stats_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(stats_kernel<128>, grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(stats_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(stats_kernel<64>, grid, block, 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(final_kernel, dim3(p.B * p.H), dim3(256), 0, stream, p);
