@@ -69,9 +69,11 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(wl, q_np, k_np, v_np, out_head0=None, budget_s=12.0):
+def cpu_baseline(wl, q_np, k_np, v_np, out_head0=None, gpu_stats=None, budget_s=12.0,
+                 bound_limit=40.0):
     """Time the oracle (as it stands) on whole query frames of head 0 until ~budget_s. With
-    the GPU output of head 0 ([S, d] float32) it also reports the parity of those rows."""
+    the GPU output of head 0 ([S, d] float32) it also reports the parity of those rows, and
+    with the GPU's per-head statistics whether the eligibility flags match the oracle's."""
     import numpy as np
 
     import oracle
@@ -109,6 +111,11 @@ def cpu_baseline(wl, q_np, k_np, v_np, out_head0=None, budget_s=12.0):
                          "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(ref)),
                          "pass": bool(np.abs(diff).max() <= 2e-2
                                       and np.linalg.norm(diff) <= 5e-3 * np.linalg.norm(ref))}
+    if gpu_stats is not None:
+        # the eligibility flags must match bit for bit (untimed: after the sample)
+        ref_st = oracle.head_stats(q_np, k_np, bound_limit=bound_limit)
+        res["eligibility_match"] = bool(np.array_equal(np.asarray(gpu_stats["eligible"]),
+                                                       ref_st["eligible"]))
     return res
 
 
@@ -417,7 +424,8 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(wl, q_np, k_np, v_np,
-                                           out[0, :, 0].float().cpu().numpy())
+                                           out[0, :, 0].float().cpu().numpy(), st,
+                                           bound_limit=args.bound_limit)
     print(json.dumps(res), flush=True)
 
 
