@@ -44,7 +44,7 @@
 // Staging: the memory-bound prologue (sfa_norms) writes V^T [b][h][d][S] into
 // the workspace (LDS transpose reads run at well under half the rate of plain
 // 16-byte reads on gfx950). K rows and V^T granules then go from HBM straight into LDS by
-// DMA (global_load_lds_dwordx4: no registers, no VALU), in NBUF rotating 64-key
+// DMA (buffer_load_dwordx4 ... lds: no registers, no VALU), in NBUF rotating 64-key
 // stages. 16-byte chunks are XOR-swizzled through the DMA source address
 // so the operand reads are free of bank conflicts:
 //   K   [key][d]            : chunk ^= key % 16 (16 lanes read 16 rows);
@@ -195,9 +195,15 @@ struct Attn {
     }
   }
 
+  // 16 bytes per lane from base + off into LDS at dst + 16 * lane, through a raw buffer
+  // resource (base in SGPRs, no range limit, 32-bit data format; off in one VGPR, below
+  // 2^32 by the host's size checks). A buffer load, unlike the global form, leaves the
+  // compiler's LDS read waits exact: while a global-segment LDS DMA is outstanding it
+  // widens every wait on an LDS read to "all of them".
   __device__ static inline void dma16(const char* base, uint32_t off, char* dst) {
-    __builtin_amdgcn_global_load_lds((global_void_ptr)(base + uint64_t(off)), (lds_void_ptr)dst,
-                                     16, 0, 0);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, -1, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)dst, 16, off, 0, 0, 0);
   }
 
   // DMA the first `ng` granules of stage s into LDS buffer `buf` (a constant
@@ -380,6 +386,19 @@ struct Attn {
     }
   }
 
+  // Region with V^T one region ahead: the 8 K reads of QK(j+1) first, then the 16 MFMAs
+  // with 3 VALU ops behind each, and the 8 reads of the next tile's V^T operand placed
+  // after the PV MFMAs that consume the same registers.
+  __device__ static inline void interleave_kv() {
+    __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // DS read: K
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i >= 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read: V^T
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+    }
+  }
+
   // Both 32-key tiles of one stage (K at kl, V^T at vl), QT == 2, fixed maximum.
   __device__ static inline void stage2_fixed(const char* lds, const Lane& L, int kl, int vl,
                                              const bf16x8 (&qf)[2][KS], f32x16 (&o)[2][DT],
@@ -473,11 +492,12 @@ struct Attn {
     if constexpr (!ONLINE && NT == 1 && NBUF == 3) {
       // Tile-level software pipeline over the N = 2*nfull full 32-key tiles:
       //   region j:  QK(j+1) + PV(j-1)  (16 MFMAs)  ||  softmax(j)  (48 VALU)
-      // with the operand reads of the region's MFMAs interleaved. Stage s (tiles
-      // 2s, 2s+1) sits in buffer s % 3; barrier B_s, just before the region that
-      // first reads stage s, waits for its DMA and then launches the DMA of stage
-      // s + 1 into the buffer of stage s - 2, whose last reader (PV of tile
-      // 2s - 3) ran in the region before B_s.
+      // Region j reads K(j+1) for its own QK and V^T(j) for the PV of region j+1,
+      // so the V^T reads have a whole region to land. Stage s (tiles 2s, 2s+1)
+      // sits in buffer s % 3; barrier B_s, just before the region that first
+      // reads stage s, waits for its DMA and then launches the DMA of stage s + 1
+      // into the buffer of stage s - 2, whose last read (V^T of tile 2s - 3, in
+      // region 2s - 3) was consumed by the PV of region 2s - 2, before B_s.
       const int N = 2 * nfull;
       f32x16(&oo)[DT] = o[0];
       if (N > 0) {
@@ -494,6 +514,7 @@ struct Attn {
         __builtin_amdgcn_sched_barrier(0);
         load_k(kf, lds, L, 32 * ROWB);
         f32x16 snext = qk(kf, qf[0]);
+        load_v(vf, lds, L, 0);  // V^T(0), used by PV(0) in region 1
         softmax_fixed(scur, mrow[0], lsum[0], pprev, p.c);
         scur = snext;
         __builtin_amdgcn_sched_barrier(0);
@@ -511,14 +532,14 @@ struct Attn {
                 issue_stage(lds, (sn + 1) % 3, L, W, X, sn + 1, sn + 1 < nfull ? 4 : rem);
             }
             const int bn = ((u + 2) / 2) % 3, tn = (u + 2) & 1;  // tile j+1 = 1 + u + 1 (mod 6)
-            const int bp = (u / 2) % 3, tp = u & 1;              // tile j-1 = 1 + u - 1 (mod 6)
+            const int bc = ((u + 1) / 2) % 3, tc = (u + 1) & 1;  // tile j = 1 + u (mod 6)
             __builtin_amdgcn_sched_barrier(0);
             load_k(kf, lds, L, bn * STAGE_B + tn * 32 * ROWB);
             snext = qk(kf, qf[0]);
-            load_v(vf, lds, L, bp * STAGE_B + tp * 2 * VG_B);
-            pv(vf, pprev, oo);
+            pv(vf, pprev, oo);                                 // V^T(j-1), read last region
+            load_v(vf, lds, L, bc * STAGE_B + tc * 2 * VG_B);  // V^T(j) for the next region
             softmax_fixed(scur, mrow[0], lsum[0], pcur, p.c);
-            interleave_16();
+            interleave_kv();
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 8; ++i) pprev[i] = pcur[i];
@@ -529,8 +550,7 @@ struct Attn {
         {
           const int jm = N - 2;  // tiles N-2 and N-1 are the two halves of stage nfull-1
           const int b = ((jm / 2) % 3);
-          load_v(vf, lds, L, b * STAGE_B);
-          pv(vf, pprev, oo);
+          pv(vf, pprev, oo);     // V^T(N-2), read in region N-2
           softmax_fixed(scur, mrow[0], lsum[0], pcur, p.c);
           load_v(vf, lds, L, b * STAGE_B + 2 * VG_B);
           pv(vf, pcur, oo);
