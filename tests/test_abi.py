@@ -137,11 +137,21 @@ def _geom(**kw):
     (dict(scale=-1.0), _lib.SFA_ERR_INVALID),
     (dict(scale=float("nan")), _lib.SFA_ERR_INVALID),
     (dict(frames=2000), _lib.SFA_ERR_UNSUPPORTED),
+    (dict(frames=1024), _lib.SFA_ERR_UNSUPPORTED),
 ])
 def test_invalid_geometry(L, kw, status):
     h = ctypes.c_void_p(123)
     assert L.sfa_plan_create(ctypes.byref(_geom(**kw)), ctypes.byref(h)) == status
     assert h.value is None
+
+
+def test_largest_frame_count_is_accepted(L):
+    # 1024 frame slots (reference + 1023 frames) is the largest per-frame table
+    h = ctypes.c_void_p()
+    assert L.sfa_plan_create(ctypes.byref(_geom(frames=1023, tokens_per_frame=16)),
+                             ctypes.byref(h)) == _lib.SFA_OK
+    assert h.value is not None
+    L.sfa_plan_destroy(h)
 
 
 def test_tile_override_errors(L):

@@ -181,6 +181,33 @@ def test_ragged_geometries(sfa, F, T, w, H, d, B, limit):
     check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
 
 
+@pytest.mark.parametrize("limit", [40.0, -1.0])
+def test_largest_frame_count(sfa, limit):
+    """1024 frame slots (reference + 1023 frames), the most a plan takes: the per-frame
+    tables at full size, on the fixed-maximum path and forced online. Sampled rows of the
+    first, last and some random frames against the oracle."""
+    F, T, w, H, d = 1023, 16, 2, 2, 64
+    say(f"[largest_frame_count] F={F} limit={limit}")
+    S = (F + 1) * T
+    g = np.random.default_rng(1023)
+    q_np = g.standard_normal((1, S, H, d)).astype(np.float32)
+    k_np = (g.standard_normal((1, S, H, d)) + 3 * g.standard_normal((1, 1, H, d))).astype(
+        np.float32)
+    v_np = g.standard_normal((1, S, H, d)).astype(np.float32)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
+    plan, out, ws = run(sfa, (1, H, d, F, T, w), q, k, v, bound_limit=limit)
+    st, _ = check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
+    assert st["eligible"].all() == (limit > 0)
+    frames = sorted({*range(4), *range(F - 3, F + 1), *g.integers(4, F - 3, 24).tolist()})
+    rows = np.array([f * T + r for f in frames for r in (0, 7, T - 1)])
+    got = out[0, torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    for h in range(H):
+        ref = oracle.attention_rows(q_np, k_np, v_np, F, T, w, 0, h, rows)
+        assert_close(got[:, h], ref, f"head {h} ({len(rows)} rows)")
+    assert torch.isfinite(out.float()).all()
+
+
 def test_zero_query_gives_window_mean(sfa):
     F, T, w, H, d = 6, 48, 1, 2, 128
     say("[zero_query]")
