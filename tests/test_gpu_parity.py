@@ -322,3 +322,31 @@ def test_head_groups_are_bitwise_equal(sfa, name, groups, nstreams):
         out, _ = sfa.attention_groups(gp, groups, q, k, v, streams=streams)
         torch.cuda.synchronize()
         assert torch.equal(out, full), rep
+
+
+@pytest.mark.parametrize("name", ["small", "720p"])
+def test_graph_replays_match_eager(sfa, name):
+    """One step (sfa_norms + sfa_fwd) captured into a HIP graph and replayed three times,
+    with eager work and a synchronisation between the replays: every replay writes the
+    eager result bit for bit (the work-queue counters are cleared by a kernel inside the
+    step, not by a memset)."""
+    wl = W.ALL[name]
+    say(f"[graph] {name}")
+    q, k, v = to_dev(*W.make_inputs_np(wl))
+    plan = sfa.Plan(*geom(wl))
+    ws = plan.workspace()
+    out = torch.empty_like(q)
+    sfa.attention(plan, q, k, v, out=out, workspace=ws)  # eager, outside the capture
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sfa.attention(plan, q, k, v, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        ws[: ws.numel() // 2].fill_(0xA5)  # eager work on the workspace between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep

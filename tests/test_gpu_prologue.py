@@ -204,3 +204,40 @@ def test_prologue_feeds_attention(sfa):
         rl = float(np.linalg.norm(dd) / np.linalg.norm(r))
         say(f"  {what}: max_abs={mx:.3e} rel_l2={rl:.3e}")
         assert mx <= ATT_MAX_ABS and rl <= ATT_REL_L2, (what, mx, rl)
+
+
+def test_layer_step_graph_replays_match_eager(sfa):
+    """Fused prologue, then norm pass and attention, captured once into a HIP graph and
+    replayed three times with eager work and a synchronisation between the replays: every
+    replay reproduces the eager q, k, v and output bit for bit."""
+    pw = replace(W.PRO_SMALL, frames=6)
+    window = 2
+    say(f"[layer_graph] {pw} w={window}")
+    x, gamma, w, cos, sin = W.make_prologue_inputs_np(pw)
+    H, d = pw.heads, pw.head_dim
+    xd, cd, sd = bf16_dev(x), f32_dev(cos), f32_dev(sin)
+    wf = sfa.prologue_fold(bf16_dev(w), bf16_dev(gamma))
+    q, k, v = sfa.qkv_prologue(xd, wf, cd, sd, H, d)
+    plan = sfa.Plan(pw.batch, H, d, pw.frames, pw.tokens_per_frame, window)
+    ws = plan.workspace()
+    out = torch.empty_like(q)
+
+    def step():
+        sfa.qkv_prologue(xd, wf, cd, sd, H, d, q=q, k=k, v=v)
+        sfa.attention(plan, q, k, v, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (q, k, v, out)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (q, k, v, out):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, r in zip((q, k, v, out), ref):
+            assert torch.equal(got, r), rep
