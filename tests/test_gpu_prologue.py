@@ -127,6 +127,13 @@ def test_prologue_matches_oracle(sfa, name):
     dict(name="pro_small", batch=2, frames=2),              # ragged: S = 624
     dict(name="pro_tiny", heads=2, head_dim=128, model_dim=64),     # one K stage
     dict(name="pro_tiny", heads=8, head_dim=64, model_dim=192, frames=10),
+    # more tiles than workgroups (each workgroup runs two or three, the next one's first
+    # K stage fetched during the last stage of the one before): odd stage count ...
+    dict(name="pro_tiny", heads=8, head_dim=64, model_dim=192, frames=31, grid_h=16, grid_w=43),
+    # ... one K stage (no overlap, stage buffers alternate between tiles) ...
+    dict(name="pro_tiny", heads=2, head_dim=128, model_dim=64, frames=31, grid_h=16, grid_w=43),
+    # ... and d = 128 with five stages, 258 tiles (two workgroups take a second one)
+    dict(name="pro_tiny", heads=4, head_dim=128, model_dim=320, frames=15, grid_h=16, grid_w=43),
 ])
 def test_prologue_shapes(sfa, case):
     case = dict(case)
