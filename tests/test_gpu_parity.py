@@ -123,6 +123,35 @@ def test_parity_sampled_full_size(sfa, name):
     assert torch.isfinite(out.float()).all()
 
 
+@pytest.mark.parametrize("limit", [40.0, -1.0])
+def test_parity_sampled_d64_batch2_many_items(sfa, limit):
+    """d = 64, two sequences, 504 work items (more than one per workgroup, so the
+    persistent workgroups' queues, stealing and counter reset run for this head size too),
+    both softmax paths; sampled rows of every (batch, head)."""
+    F, T, w, H, d, B = 13, 720, 2, 6, 64, 2
+    say(f"[d64_batch2] limit={limit}")
+    S = (F + 1) * T
+    g = np.random.default_rng(64)
+    q_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    k_np = (g.standard_normal((B, S, H, d)) + 3 * g.standard_normal((B, 1, H, d))).astype(
+        np.float32)
+    v_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
+    plan, out, ws = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit)
+    assert plan.info["items"] == B * H * (F + 1) * (T // 240)
+    st, _ = check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
+    assert st["eligible"].all() == (limit > 0)
+    rows = np.array(sorted({f * T + r for f in range(F + 1) for r in (0, 239, 240, T - 1)}
+                           | set(g.integers(0, S, 16).tolist())))
+    got_all = out[:, torch.from_numpy(rows).cuda()].float().cpu().numpy()   # [B, R, H, d]
+    for b in range(B):
+        for h in range(H):
+            ref = oracle.attention_rows(q_np, k_np, v_np, F, T, w, b, h, rows)
+            assert_close(got_all[b, :, h], ref, f"b {b} head {h} ({len(rows)} rows)")
+    assert torch.isfinite(out.float()).all()
+
+
 def test_full_size_frame_indicator_has_no_mass_outside_window(sfa):
     """720p shape, every row: with v_j = one-hot(frame(j)) the output is exactly zero on
     frames outside the row's window and sums to ~1 (any size, no oracle needed)."""
@@ -350,3 +379,35 @@ def test_graph_replays_match_eager(sfa, name):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), rep
+
+
+# (B, H, d, F, T, w): the small workload, and d = 64 with two sequences and 5-granule frames
+OPTION_GEOMS = [(1, 8, 128, 8, 208, 2), (2, 2, 64, 6, 80, 1)]
+
+
+@pytest.mark.parametrize("geom_", OPTION_GEOMS)
+@pytest.mark.parametrize("opts", [dict(waves=8, lds_stages=2), dict(waves=8, lds_stages=4),
+                                  dict(waves=4, lds_stages=2), dict(waves=4, lds_stages=3),
+                                  dict(waves=4, lds_stages=4), dict(block_q=16)])
+@pytest.mark.parametrize("limit", [40.0, -1.0])
+def test_plan_options_parity(sfa, geom_, opts, limit):
+    """Every launch configuration sfa_plan_create_ex offers (4 waves of two query tiles, two
+    or four LDS stages, one-granule query blocks), both softmax paths, against the oracle."""
+    B, H, d, F, T, w = geom_
+    say(f"[plan_options] {geom_} {opts} limit={limit}")
+    S = (F + 1) * T
+    g = np.random.default_rng(B * 100 + T)
+    q_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    k_np = (g.standard_normal((B, S, H, d)) + 3 * g.standard_normal((B, 1, H, d))).astype(
+        np.float32)
+    v_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
+    plan, out, ws = run(sfa, geom_, q, k, v, bound_limit=limit, **opts)
+    if "block_q" in opts:
+        assert plan.info["block_q"] == opts["block_q"]
+    if "waves" in opts:
+        assert plan.info["waves_per_item"] == opts["waves"]
+    ref = oracle.attention(q_np, k_np, v_np, F, T, w)
+    assert_close(out.float().cpu().numpy(), ref, "options")
+    check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
