@@ -105,11 +105,20 @@ def _ws(plan, workspace, device):
     return workspace
 
 
+def _ws_args(ws):
+    """(pointer, size in bytes) of a workspace tensor, which must be a device tensor."""
+    if not ws.is_cuda:
+        raise TypeError("the workspace must be a device tensor")
+    if not ws.is_contiguous():
+        raise ValueError("the workspace must be contiguous")
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
 def sfa_norms(plan: Plan, q, k, v, workspace=None, stream=None):
     """Prologue: norm array (from q, k) and V^T staging (from v) into the workspace."""
     ws = _ws(plan, workspace, q.device)
     check(lib().sfa_norms(plan.handle, as_tensor(q, plan, "q"), as_tensor(k, plan, "k"),
-                          as_tensor(v, plan, "v"), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                          as_tensor(v, plan, "v"), *_ws_args(ws),
                           _stream_ptr(stream)), "sfa_norms")
     return ws
 
@@ -123,7 +132,7 @@ def sfa_fwd(plan: Plan, q, k, v, out=None, workspace=None, stream=None):
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     check(lib().sfa_fwd(plan.handle, as_tensor(q, plan, "q"), as_tensor(k, plan, "k"),
                         as_tensor(v, plan, "v"), as_tensor(out, plan, "o"),
-                        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                        *_ws_args(workspace),
                         _stream_ptr(stream)), "sfa_fwd")
     return out
 
@@ -137,7 +146,7 @@ def sfa_attention(plan: Plan, q, k, v, out=None, workspace=None, stream=None):
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     check(lib().sfa_attention(plan.handle, as_tensor(q, plan, "q"), as_tensor(k, plan, "k"),
                               as_tensor(v, plan, "v"), as_tensor(out, plan, "o"),
-                              ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)),
+                              *_ws_args(ws), _stream_ptr(stream)),
           "sfa_attention")
     return out, ws
 
@@ -163,7 +172,7 @@ def sfa_attention_groups(group_plan: Plan, groups: int, q, k, v, out=None, works
     ts = [Tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2)) for t in (q, k, v, out)]
     arr = (ctypes.c_void_p * max(1, len(streams)))(*[s.cuda_stream for s in streams])
     check(lib().sfa_attention_groups(group_plan.handle, groups, *ts,
-                                     ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                     *_ws_args(workspace),
                                      _stream_ptr(stream), arr, len(streams)),
           "sfa_attention_groups")
     return out, workspace
@@ -218,11 +227,15 @@ def sfa_prologue_fold(w, gamma, stream=None):
     import torch
 
     if w.dtype != torch.bfloat16 or gamma.dtype != torch.bfloat16 or w.dim() != 2 or \
-            not w.is_contiguous() or tuple(gamma.shape) != (w.shape[1],):
-        raise ValueError("w must be a contiguous bf16 [N, C] tensor and gamma bf16 [C]")
+            not w.is_contiguous() or tuple(gamma.shape) != (w.shape[1],) or \
+            not gamma.is_contiguous():
+        raise ValueError("w must be a contiguous bf16 [N, C] tensor and gamma a contiguous "
+                         "bf16 [C] tensor")
+    if not (w.is_cuda and gamma.is_cuda):
+        raise TypeError("w and gamma must be device tensors")
     out = torch.empty_like(w)
     check(lib().sfa_prologue_fold(ctypes.c_void_p(w.data_ptr()),
-                                  ctypes.c_void_p(gamma.contiguous().data_ptr()),
+                                  ctypes.c_void_p(gamma.data_ptr()),
                                   ctypes.c_void_p(out.data_ptr()), w.shape[0], w.shape[1],
                                   _stream_ptr(stream)), "sfa_prologue_fold")
     return out
@@ -238,6 +251,10 @@ def sfa_qkv_prologue(x, w_folded, cos, sin, heads: int, head_dim: int, eps: floa
     B, S, C = x.shape
     if x.dtype != torch.bfloat16 or x.stride(2) != 1:
         raise ValueError("x must be bf16 [B, S, C] with C contiguous")
+    for name, t in (("x", x), ("w_folded", w_folded), ("cos", cos), ("sin", sin)) + \
+            tuple((n, t) for n, t in (("q", q), ("k", k), ("v", v)) if t is not None):
+        if not t.is_cuda:
+            raise TypeError(f"{name} must be a device tensor")
     if w_folded.dtype != torch.bfloat16 or tuple(w_folded.shape) != (3 * heads * head_dim, C) \
             or not w_folded.is_contiguous():
         raise ValueError("w_folded must be a contiguous bf16 [3*H*d, C] tensor")
@@ -318,7 +335,7 @@ def sfa_generic_attention(plan: GenericPlan, q, k, v, out=None, workspace=None, 
     check(lib().sfa_generic_attention(plan.handle, as_tensor(q, plan, "q"),
                                       as_tensor(k, plan, "k"), as_tensor(v, plan, "v"),
                                       as_tensor(out, plan, "o"),
-                                      ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                      *_ws_args(workspace),
                                       _stream_ptr(stream)), "sfa_generic_attention")
     return out, workspace
 

@@ -335,3 +335,23 @@ def test_prologue_call_validation_happens_before_any_launch(L):
     assert Q(g, x, w, cs, sn, outs[0], null_out, outs[2], None) == _lib.SFA_ERR_INVALID
     on_x = _lib.Tensor((1 << 20) + 64, S * H * d, H * d, d)       # output aliasing x
     assert Q(g, x, w, cs, sn, outs[0], on_x, outs[2], None) == _lib.SFA_ERR_INVALID
+
+
+def test_binding_rejects_host_tensors():
+    """The binding refuses host tensors before anything reaches the library (a host pointer
+    handed to a kernel would fault the device)."""
+    torch = pytest.importorskip("torch")
+    import sparse_attention_frame_amd as sfa
+
+    w = torch.zeros(3 * 2 * 128, 64, dtype=torch.bfloat16)
+    gamma = torch.ones(64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        sfa.prologue_fold(w, gamma)
+    x = torch.zeros(1, 16, 64, dtype=torch.bfloat16)
+    cos, sin = torch.zeros(16, 64), torch.zeros(16, 64)
+    with pytest.raises(TypeError):
+        sfa.qkv_prologue(x, w, cos, sin, 2, 128)
+    plan = sfa.Plan(1, 2, 64, 0, 16, 0)
+    q = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        sfa.attention(plan, q, q, q)
