@@ -187,7 +187,7 @@ def sfa_read_head_stats(plan: Plan, workspace, stream=None):
     bound = np.empty((g.batch, g.heads), np.float32)
     elig = np.empty((g.batch, g.heads), np.uint8)
     f = ctypes.POINTER(ctypes.c_float)
-    check(lib().sfa_read_head_stats(plan.handle, ctypes.c_void_p(workspace.data_ptr()),
+    check(lib().sfa_read_head_stats(plan.handle, _ws_args(workspace)[0],
                                     mu.ctypes.data_as(f), kmax.ctypes.data_as(f),
                                     qmax.ctypes.data_as(f), bound.ctypes.data_as(f),
                                     elig.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
@@ -201,7 +201,7 @@ def sfa_read_row_norms(plan: Plan, workspace, stream=None):
     qn = np.empty((g.batch, g.heads, plan.seq), np.float32)
     qmu = np.empty((g.batch, g.heads, plan.seq), np.float32)
     f = ctypes.POINTER(ctypes.c_float)
-    check(lib().sfa_read_row_norms(plan.handle, ctypes.c_void_p(workspace.data_ptr()),
+    check(lib().sfa_read_row_norms(plan.handle, _ws_args(workspace)[0],
                                    qn.ctypes.data_as(f), qmu.ctypes.data_as(f),
                                    _stream_ptr(stream)), "sfa_read_row_norms")
     return qn, qmu
@@ -215,7 +215,7 @@ def sfa_read_frame_stats(plan: Plan, workspace, stream=None):
     bound = np.empty(shape, np.float32)
     elig = np.empty(shape, np.uint8)
     f = ctypes.POINTER(ctypes.c_float)
-    check(lib().sfa_read_frame_stats(plan.handle, ctypes.c_void_p(workspace.data_ptr()),
+    check(lib().sfa_read_frame_stats(plan.handle, _ws_args(workspace)[0],
                                      kvis.ctypes.data_as(f), bound.ctypes.data_as(f),
                                      elig.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
                                      _stream_ptr(stream)), "sfa_read_frame_stats")
