@@ -411,3 +411,41 @@ def test_plan_options_parity(sfa, geom_, opts, limit):
     ref = oracle.attention(q_np, k_np, v_np, F, T, w)
     assert_close(out.float().cpu().numpy(), ref, "options")
     check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
+
+
+def _random_cases(n=24, seed=2024):
+    """Seeded geometries and plan options: frames 0-18, 1-10 granules per frame, windows 0-5
+    (also past both ends), 1-3 heads, d 64 / 128, one or two sequences, any launch option."""
+    g = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        F = int(g.integers(0, 19))
+        T = 16 * int(g.integers(1, 11))
+        w = int(g.integers(0, 6))
+        H = int(g.integers(1, 4))
+        d = int(g.choice([64, 128]))
+        B = int(g.integers(1, 3))
+        waves = int(g.choice([0, 4, 8]))
+        stages = int(g.choice([0, 2, 3, 4]))
+        limit = float(g.choice([40.0, -1.0, 40.0]))
+        cases.append((F, T, w, H, d, B, waves, stages, limit))
+    return cases
+
+
+@pytest.mark.parametrize("F,T,w,H,d,B,waves,stages,limit", _random_cases())
+def test_random_geometries_and_options(sfa, F, T, w, H, d, B, waves, stages, limit):
+    say(f"[random] F={F} T={T} w={w} H={H} d={d} B={B} waves={waves} stages={stages} "
+        f"limit={limit}")
+    S = (F + 1) * T
+    g = np.random.default_rng(F * 7919 + T * 31 + w * 7 + H + d + B)
+    q_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    k_np = (g.standard_normal((B, S, H, d)) + 3 * g.standard_normal((B, 1, H, d))).astype(
+        np.float32)
+    v_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
+    plan, out, ws = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit, waves=waves,
+                        lds_stages=stages)
+    ref = oracle.attention(q_np, k_np, v_np, F, T, w)
+    assert_close(out.float().cpu().numpy(), ref, "random")
+    check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
