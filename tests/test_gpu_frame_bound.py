@@ -166,3 +166,35 @@ def test_frame_bound_ragged(sfa, F, T, w, H, d, B, limit):
     check_frame_stats(sfa, plan, ws, wl, q_np, k_np, 1, limit)
     ref = oracle.attention(q_np, k_np, v_np, F, T, w)
     assert_close(out.float().cpu().numpy(), ref, "frame bound ragged")
+
+
+def _random_geoms(n=12, seed=777):
+    g = np.random.default_rng(seed)
+    return [(int(g.integers(0, 19)), 16 * int(g.integers(1, 11)), int(g.integers(0, 6)),
+             int(g.integers(1, 4)), int(g.choice([64, 128])), int(g.integers(1, 3)),
+             float(g.choice([40.0, 12.0, -1.0])), float(g.choice([1.0, 6.0])))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("F,T,w,H,d,B,limit,boost", _random_geoms())
+def test_frame_bound_random_geometries(sfa, F, T, w, H, d, B, limit, boost):
+    """Seeded random geometries with the per-visible-frame bound; the last frame's keys
+    optionally scaled up (outliers), limits that put some, all or no query frames online."""
+    say(f"[frame_bound_random] F={F} T={T} w={w} H={H} d={d} B={B} limit={limit} "
+        f"boost={boost}")
+    S = (F + 1) * T
+    g = np.random.default_rng(F * 313 + T * 7 + w + H + d + B)
+    q_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    k_np = (g.standard_normal((B, S, H, d)) + 3 * g.standard_normal((B, 1, H, d))).astype(
+        np.float32)
+    k_np[:, F * T:] *= boost
+    v_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
+    wl = W.Workload("random", F, T, H, d, w, 3.0, 0, batch=B)
+    plan = sfa.Plan(B, H, d, F, T, w, bound_limit=limit, bound_mode=1)
+    out, ws = sfa.attention(plan, q, k, v)
+    torch.cuda.synchronize()
+    check_frame_stats(sfa, plan, ws, wl, q_np, k_np, 1, limit)
+    ref = oracle.attention(q_np, k_np, v_np, F, T, w)
+    assert_close(out.float().cpu().numpy(), ref, "frame bound random")

@@ -101,3 +101,30 @@ def test_generic_sampled_full_size(sfa, name):
         ref = oracle.attention_rows(q_np, k_np, v_np, wl.frames, T, wl.window, 0, h, rows)
         assert_close(got[:, h], ref, f"generic {name} head {h}")
     assert torch.isfinite(out.float()).all()
+
+
+def _random_geoms(n=12, seed=4242):
+    g = np.random.default_rng(seed)
+    return [(int(g.integers(0, 19)), 16 * int(g.integers(1, 21)), int(g.integers(0, 6)),
+             int(g.integers(1, 4)), int(g.choice([64, 128])), int(g.integers(1, 3)))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("F,T,w,H,d,B", _random_geoms())
+def test_generic_random_geometries(sfa, F, T, w, H, d, B):
+    """Seeded random geometries: frame spans of 1-20 granules (rarely a multiple of the
+    256 x 128 tiles, so most blocks near frame edges are partial), windows 0-5."""
+    say(f"[generic_random] F={F} T={T} w={w} H={H} d={d} B={B}")
+    S = (F + 1) * T
+    g = np.random.default_rng(F * 131 + T * 17 + w + H + d + B)
+    q_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    k_np = (g.standard_normal((B, S, H, d)) + 3 * g.standard_normal((B, 1, H, d))).astype(
+        np.float32)
+    v_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
+    plan = sfa.GenericPlan(B, H, d, F, T, w)
+    out, _ = sfa.generic_attention(plan, q, k, v)
+    torch.cuda.synchronize()
+    ref = oracle.attention(q_np, k_np, v_np, F, T, w)
+    assert_close(out.float().cpu().numpy(), ref, "generic random")
