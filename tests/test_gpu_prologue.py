@@ -248,3 +248,27 @@ def test_layer_step_graph_replays_match_eager(sfa):
         torch.cuda.synchronize()
         for got, r in zip((q, k, v, out), ref):
             assert torch.equal(got, r), rep
+
+
+def _random_shapes(n=10, seed=99):
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(g.choice([64, 128]))
+        heads = int(g.choice([4, 8, 12])) if d == 64 else int(g.choice([2, 4, 6]))
+        out.append(dict(name="pro_tiny", batch=int(g.integers(1, 3)), frames=int(g.integers(0, 12)),
+                        grid_h=int(g.integers(1, 20)), grid_w=int(g.integers(1, 30)),
+                        heads=heads, head_dim=d, model_dim=64 * int(g.integers(1, 9))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_shapes())
+def test_prologue_random_shapes(sfa, case):
+    """Seeded random shapes: any sequence length (ragged last token tile), 1-8 K stages,
+    d 64 / 128, one or two sequences."""
+    case = dict(case)
+    pw = replace(W.PROLOGUE[case.pop("name")], **case)
+    say(f"[prologue_random] {pw}")
+    x, gamma, w, cos, sin = W.make_prologue_inputs_np(pw)
+    q, k, v = run(sfa, pw, x, gamma, w, cos, sin)
+    check_against_oracle(q, k, v, pw, x, gamma, w, cos, sin)
