@@ -72,12 +72,14 @@ typedef struct sfa_plan_info {
   int32_t block_q;          /* query rows per work item; divides T, multiple of 16 */
   int32_t granule;          /* token granule of the key loop (16) */
   int32_t waves_per_item;   /* 64-lane waves in one workgroup */
-  int32_t items;            /* work items = B * H * (F + 1) * (T / block_q) */
+  int32_t items;            /* work items = B * H * (F + 1 + split_frames) * (T / block_q) */
   int64_t active_pairs;     /* visible (query, key) pairs summed over B and H */
   double active_flops;      /* 4 * d * active_pairs (q.k and p.v, 2 flops per MAC) */
   int64_t io_bytes;         /* q, k, v read once and o written once: 8 * B * S * H * d */
   size_t workspace_bytes;   /* device workspace needed by sfa_norms / sfa_fwd */
   int32_t bound_mode;       /* the plan's bound_mode (see sfa_plan_options) */
+  int32_t split_frames;     /* query frames whose work items run as two key halves (see
+                               sfa_plan_options.key_split) */
 } sfa_plan_info;
 
 /* Validates the geometry and builds the work decomposition (host only, no HIP
@@ -100,6 +102,13 @@ typedef struct sfa_plan_options {
                              that query frame sees (reference frame + window, section
                              "Deleting the mask"), one flag per query frame. Never looser
                              than 0; the output is the same softmax either way. */
+  int32_t key_split;      /* 0 (default): with 8 waves per item, the items of the query
+                             frames that see the fewest frames (more than one) run as two
+                             key halves, whose partial outputs and row sums the later
+                             finisher merges (section "Unchaining softmax": with a shared
+                             fixed maximum the halves simply add); they are the last long
+                             items of the largest-first order, so the launch's tail gets
+                             shorter. -1: never split. */
 } sfa_plan_options;
 
 /* sfa_plan_create with overrides (options may be NULL). Values outside the
@@ -123,6 +132,13 @@ int sfa_plan_key_ranges(const sfa_plan* plan, int32_t query_frame, int32_t range
  * decreasing key count (largest first) and grouped so that the items sharing
  * one (batch, head, frame) key stream land on one XCD. */
 int sfa_plan_item(const sfa_plan* plan, int32_t index, int32_t item[4]);
+
+/* Keys of the work item at `index`: *half is -1 for an item that covers every visible
+ * key of its query frame, 0 or 1 for the first or second key half of a split one (the
+ * visible frames, reference frame first, cut after the first ceil(n/2)); its key token
+ * ranges as half-open [start, end) pairs in ranges[0..2*n), n = 1 or 2. */
+int sfa_plan_item_keys(const sfa_plan* plan, int32_t index, int32_t* half, int32_t ranges[4],
+                       int32_t* n);
 
 /* Memory-bound prologue of the attention, written into `workspace` only:
  *  - the norm array of the fixed maximum (section "Unchaining softmax"): per

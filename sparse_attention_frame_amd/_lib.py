@@ -28,7 +28,8 @@ class Tensor(ctypes.Structure):
 
 class PlanOptions(ctypes.Structure):
     _fields_ = [("block_q", ctypes.c_int32), ("waves_per_item", ctypes.c_int32),
-                ("lds_stages", ctypes.c_int32), ("bound_mode", ctypes.c_int32)]
+                ("lds_stages", ctypes.c_int32), ("bound_mode", ctypes.c_int32),
+                ("key_split", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -36,7 +37,7 @@ class PlanInfo(ctypes.Structure):
                 ("waves_per_item", ctypes.c_int32), ("items", ctypes.c_int32),
                 ("active_pairs", ctypes.c_int64), ("active_flops", ctypes.c_double),
                 ("io_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
-                ("bound_mode", ctypes.c_int32)]
+                ("bound_mode", ctypes.c_int32), ("split_frames", ctypes.c_int32)]
 
 
 class GenericInfo(ctypes.Structure):
@@ -55,7 +56,7 @@ class PrologueGeometry(ctypes.Structure):
 # every symbol include/sfa.h declares
 EXPORTS = (
     "sfa_plan_create", "sfa_plan_create_ex", "sfa_plan_destroy", "sfa_plan_get_info",
-    "sfa_plan_key_ranges", "sfa_plan_item", "sfa_norms", "sfa_fwd", "sfa_attention",
+    "sfa_plan_key_ranges", "sfa_plan_item", "sfa_plan_item_keys", "sfa_norms", "sfa_fwd", "sfa_attention",
     "sfa_attention_groups", "sfa_read_head_stats", "sfa_read_row_norms", "sfa_read_frame_stats",
     "sfa_prologue_fold", "sfa_qkv_prologue",
     "sfa_generic_create", "sfa_generic_destroy", "sfa_generic_get_info", "sfa_generic_block_class",
@@ -85,6 +86,7 @@ def _declare(lib):
         "sfa_plan_get_info": (ctypes.c_int, [P, ctypes.POINTER(PlanInfo)]),
         "sfa_plan_key_ranges": (ctypes.c_int, [P, ctypes.c_int32, i32p, i32p]),
         "sfa_plan_item": (ctypes.c_int, [P, ctypes.c_int32, i32p]),
+        "sfa_plan_item_keys": (ctypes.c_int, [P, ctypes.c_int32, i32p, i32p, i32p]),
         "sfa_norms": (ctypes.c_int, [P, Tensor, Tensor, Tensor, P, ctypes.c_size_t, P]),
         "sfa_fwd": (ctypes.c_int, [P, Tensor, Tensor, Tensor, Tensor, P, ctypes.c_size_t, P]),
         "sfa_attention": (ctypes.c_int, [P, Tensor, Tensor, Tensor, Tensor, P, ctypes.c_size_t,

@@ -31,13 +31,13 @@ class Plan:
     def __init__(self, batch: int, heads: int, head_dim: int, frames: int,
                  tokens_per_frame: int, window: int, scale: float = 0.0,
                  bound_limit: float = 40.0, block_q: int = 0, waves: int = 0,
-                 lds_stages: int = 0, bound_mode: int = 0):
+                 lds_stages: int = 0, bound_mode: int = 0, key_split: int = 0):
         self.geometry = Geometry(batch, heads, head_dim, frames, tokens_per_frame, window,
                                  scale, bound_limit)
         handle = ctypes.c_void_p()
         L = lib()
-        if block_q or waves or lds_stages or bound_mode:
-            opts = PlanOptions(block_q, waves, lds_stages, bound_mode)
+        if block_q or waves or lds_stages or bound_mode or key_split:
+            opts = PlanOptions(block_q, waves, lds_stages, bound_mode, key_split)
             st = L.sfa_plan_create_ex(ctypes.byref(self.geometry), ctypes.byref(opts),
                                       ctypes.byref(handle))
         else:
@@ -75,6 +75,15 @@ class Plan:
         out = (ctypes.c_int32 * 4)()
         check(lib().sfa_plan_item(self._h, index, out), "sfa_plan_item")
         return tuple(out)
+
+    def item_keys(self, index: int):
+        """(half, [(start, end), ...]): half -1 for a whole item, 0 / 1 for a key half."""
+        half = ctypes.c_int32()
+        r = (ctypes.c_int32 * 4)()
+        n = ctypes.c_int32()
+        check(lib().sfa_plan_item_keys(self._h, index, ctypes.byref(half), r, ctypes.byref(n)),
+              "sfa_plan_item_keys")
+        return half.value, [(r[2 * i], r[2 * i + 1]) for i in range(n.value)]
 
     def workspace(self, device=None):
         import torch

@@ -69,6 +69,8 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   if (stages < 2 || stages > 4) return SFA_ERR_UNSUPPORTED;
   const int bound_mode = opt ? opt->bound_mode : 0;
   if (bound_mode != 0 && bound_mode != 1) return SFA_ERR_UNSUPPORTED;
+  const int key_split = opt ? opt->key_split : 0;
+  if (key_split != 0 && key_split != -1) return SFA_ERR_UNSUPPORTED;
   int gq;
   if (block_q == 0) {
     gq = auto_block_granules(tg);
@@ -91,14 +93,49 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   p->stages = stages;
   p->bound_mode = bound_mode;
   p->nqb = tg / gq;
-  p->items = B * H * (F + 1) * p->nqb;
   p->nchunk = (p->S + kNormChunk - 1) / kNormChunk;
 
-  // frames by decreasing cost (number of visible frames), ties by frame index
-  for (int f = 0; f <= F; ++f) p->frame_order[f] = uint16_t(f);
-  std::stable_sort(p->frame_order, p->frame_order + F + 1, [&](uint16_t a, uint16_t b) {
-    return visible_frames(a, F, w) > visible_frames(b, F, w);
-  });
+  // Key split of the tail: the items of the cheapest query frames that see more than
+  // one frame are the last multi-frame items the largest-first order starts, and the
+  // longest of the short items that end the launch; each is split into two key halves
+  // (frames ordered reference first), so the tail is made of items half as long. Only
+  // the 8-wave kernel (one 32-row query tile per wave) merges halves.
+  int vmin = 0;
+  if (key_split == 0 && waves == 8)
+    for (int f = 1; f <= F; ++f) {
+      const int v = visible_frames(f, F, w);
+      if (v >= 2 && (vmin == 0 || v < vmin)) vmin = v;
+    }
+  int nsplit = 0;
+  if (vmin > 0)
+    for (int f = 1; f <= F; ++f) nsplit += visible_frames(f, F, w) == vmin;
+  if (nsplit > kMaxSplitFrames || F + 1 + nsplit > kMaxFrameSlots) nsplit = 0;
+  // slots: every query frame once, a split one as two halves; by decreasing cost (number
+  // of visible frames of the slot), ties in slot order
+  int cost[kMaxFrameSlots];
+  int ns = 0, si = 0;
+  for (int f = 0; f <= F; ++f) {
+    const int v = visible_frames(f, F, w);
+    if (nsplit > 0 && f > 0 && v == vmin) {
+      p->frame_order[ns] = uint16_t(f | (1 << 10) | (si << 12));
+      cost[ns++] = (v + 1) / 2;
+      p->frame_order[ns] = uint16_t(f | (2 << 10) | (si << 12));
+      cost[ns++] = v / 2;
+      ++si;
+    } else {
+      p->frame_order[ns] = uint16_t(f);
+      cost[ns++] = v;
+    }
+  }
+  int idx[kMaxFrameSlots];
+  for (int i = 0; i < ns; ++i) idx[i] = i;
+  std::stable_sort(idx, idx + ns, [&](int a, int b) { return cost[a] > cost[b]; });
+  uint16_t sorted[kMaxFrameSlots];
+  for (int i = 0; i < ns; ++i) sorted[i] = p->frame_order[idx[i]];
+  memcpy(p->frame_order, sorted, sizeof(uint16_t) * ns);
+  p->nslots = ns;
+  p->nsplit = nsplit;
+  p->items = B * H * ns * p->nqb;
   int64_t frame_pairs = 0;
   for (int f = 0; f <= F; ++f) frame_pairs += visible_frames(f, F, w);
   p->active_pairs = frame_pairs * int64_t(T) * T * B * H;
@@ -127,6 +164,9 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   p->ws.pqmax = take(ngran * bh * 4);
   p->ws.vt = take(bh * size_t(D) * size_t(p->S) * 2);  // bf16 V^T [b][h][d][S]
   p->ws.queue = take(kQueueWords * 4);
+  const size_t nsplit_items = size_t(nsplit) * bh * p->nqb;
+  p->ws.part = take(nsplit_items * 2 * part_floats(D) * 4);
+  p->ws.split_cnt = take(nsplit_items * 4);
   p->ws.total = off;
   *out = p;
   return SFA_OK;
@@ -181,6 +221,8 @@ NormParams norm_params(const sfa_plan* p, const sfa_tensor& q, const sfa_tensor&
   n.pkmax = reinterpret_cast<float*>(base + p->ws.pkmax);
   n.pqmax = reinterpret_cast<float*>(base + p->ws.pqmax);
   n.queue = reinterpret_cast<int32_t*>(base + p->ws.queue);
+  n.split_cnt = reinterpret_cast<int32_t*>(base + p->ws.split_cnt);
+  n.nsplit_cnt = p->nsplit * p->g.batch * p->g.heads * p->nqb;
   n.B = p->g.batch; n.H = p->g.heads; n.S = p->S; n.D = p->g.head_dim;
   n.nchunk = p->nchunk;
   n.T = p->g.tokens_per_frame; n.F = p->g.frames; n.w = p->g.window;
@@ -454,6 +496,7 @@ int sfa_plan_get_info(const sfa_plan* p, sfa_plan_info* out) {
   out->io_bytes = int64_t(8) * p->g.batch * p->S * p->g.heads * p->g.head_dim;
   out->workspace_bytes = p->ws.total;
   out->bound_mode = p->bound_mode;
+  out->split_frames = p->nsplit;
   return SFA_OK;
 }
 
@@ -481,6 +524,29 @@ int sfa_plan_item(const sfa_plan* p, int32_t index, int32_t item[4]) {
   item[1] = it.h;
   item[2] = it.f;
   item[3] = it.qb;
+  return SFA_OK;
+}
+
+int sfa_plan_item_keys(const sfa_plan* p, int32_t index, int32_t* half, int32_t ranges[4],
+                       int32_t* n) {
+  if (!p || !half || !ranges || !n || index < 0 || index >= p->items) return SFA_ERR_INVALID;
+  const Item it = decode_item(index, p->frame_order, p->g.batch, p->g.heads, p->nqb, p->items);
+  const int F = p->g.frames, T = p->g.tokens_per_frame, w = p->g.window;
+  const KeyRanges r = it.half < 0 ? key_ranges(it.f, F, T, w) : half_key_ranges(it.f, it.half, F, T, w);
+  *half = it.half;
+  int m = 0;
+  if (r.r0_end > 0) {
+    ranges[2 * m] = 0;
+    ranges[2 * m + 1] = r.r0_end;
+    ++m;
+  }
+  if (r.r1_end > r.r1_begin) {
+    ranges[2 * m] = r.r1_begin;
+    ranges[2 * m + 1] = r.r1_end;
+    ++m;
+  }
+  for (int i = 2 * m; i < 4; ++i) ranges[i] = 0;
+  *n = m;
   return SFA_OK;
 }
 
@@ -529,6 +595,8 @@ int sfa_fwd(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_ten
   f.gq = p->gq; f.nqb = p->nqb; f.items = p->items;
   f.c = p->scale * 1.4426950408889634f;
   f.queue = reinterpret_cast<int32_t*>(base + p->ws.queue);
+  f.part = reinterpret_cast<float*>(base + p->ws.part);
+  f.split_cnt = reinterpret_cast<int32_t*>(base + p->ws.split_cnt);
   memcpy(f.frame_order, p->frame_order, sizeof(f.frame_order));
   return hip_status(
       sfa_launch_fwd(f, p->g.head_dim, p->waves, p->stages, static_cast<hipStream_t>(stream)));

@@ -443,7 +443,8 @@ struct Attn {
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
-    const KeyRanges r = sfa::key_ranges(it.f, p.F, p.T, p.w);
+    const KeyRanges r = it.half < 0 ? sfa::key_ranges(it.f, p.F, p.T, p.w)
+                                    : sfa::half_key_ranges(it.f, it.half, p.F, p.T, p.w);
     const int ngran = (r.r0_end + (r.r1_end - r.r1_begin)) / 16;
     const char* kb = reinterpret_cast<const char*>(p.k + it.b * p.ksb + it.h * p.ksh);
     const char* vtb =
@@ -621,6 +622,11 @@ struct Attn {
 
     }
 
+    if (it.half >= 0) {  // a key half (the plan splits 8-wave items only: NT == 1)
+      if constexpr (NT == 1 && QT == 1) merge_halves(p, it, o[0], lsum[0], mrow[0], rows, row0);
+      return;
+    }
+
     // epilogue: the two lane halves hold the two key halves of every row
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -640,6 +646,84 @@ struct Attn {
           }
       }
     }
+  }
+
+  // Epilogue of one key half of a split item. The half leaves its partial output O
+  // (not normalised), row sum l and the maximum m they are relative to in the
+  // workspace, then counts itself in; the half that comes second reads the other's
+  // partial and writes O = (O_0 s_0 + O_1 s_1) / (l_0 s_0 + l_1 s_1) with
+  // s_h = 2^(m_h - max(m_0, m_1)) (s_h = 1 for a shared fixed maximum), always in half
+  // order, so the result does not depend on which half finished first. The halves may
+  // run on different XCDs, whose L2 caches are not coherent with each other: the partial
+  // goes out with device-scope (write-through) stores, every one of them acknowledged
+  // before the count, and the second half reads it with device-scope loads. A device-scope
+  // fence would do the same by writing back and invalidating the whole L2 of the XCD,
+  // which costs its other workgroups their cached K and V^T. The second half clears the
+  // count for the next launch.
+  __device__ static void merge_halves(const FwdParams& p, const Item& it, const f32x16 (&o)[DT],
+                                      float lpart, float m, int rows, int row0) {
+    constexpr int PF = sfa::part_floats(D);
+    constexpr int WF = DT * 16 * 64;  // floats of one wave's O
+    constexpr int OL = 8 * WF;        // l of 256 rows, then m
+    __shared__ int split_seen;
+    // thread index re-read here (an empty asm the compiler cannot see through), so that
+    // these lane addresses are not hoisted out of the item loop, where they would stay
+    // live across the key loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+    const float l = lpart + __shfl_xor(lpart, 32, 64);
+    const int slot = ((it.split * p.B + it.b) * p.H + it.h) * p.nqb + it.qb;
+    float* mine = p.part + (int64_t(slot) * 2 + it.half) * PF;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        __hip_atomic_store(&mine[wave * WF + (dt * 16 + i) * 64 + lane], o[dt][i],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int row = wave * 32 + l32;
+    if (g == 0) {
+      __hip_atomic_store(&mine[OL + row], l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&mine[OL + 256 + row], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vm<0>();  // every store of this wave acknowledged
+    __syncthreads();
+    if (tid == 0) split_seen = atomicAdd(&p.split_cnt[slot], 1);
+    __syncthreads();
+    const int first = split_seen == 0;
+    __syncthreads();
+    if (first) return;
+    if (tid == 0) atomicExch(&p.split_cnt[slot], 0);
+    float* other = p.part + (int64_t(slot) * 2 + (1 - it.half)) * PF;
+    const float lo = __hip_atomic_load(&other[OL + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float mo = __hip_atomic_load(&other[OL + 256 + row], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    const bool h0 = it.half == 0;
+    const float m0 = h0 ? m : mo, m1 = h0 ? mo : m;
+    const float l0 = h0 ? l : lo, l1 = h0 ? lo : l;
+    const float mm = fmaxf(m0, m1);
+    const float s0 = __builtin_amdgcn_exp2f(m0 - mm), s1 = __builtin_amdgcn_exp2f(m1 - mm);
+    const float inv = 1.0f / (l0 * s0 + l1 * s1);
+    if (row >= rows) return;
+    uint16_t* op = p.o + it.b * p.osb + int64_t(row0 + row) * p.oss + it.h * p.osh + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * q4 + u;
+          const float a = o[dt][i];
+          const float b = __hip_atomic_load(&other[wave * WF + (dt * 16 + i) * 64 + lane],
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          y[u] = ((h0 ? a : b) * s0 + (h0 ? b : a) * s1) * inv;
+        }
+        uint2 wv;
+        wv.x = pack_bf16x2(y[0], y[1]);
+        wv.y = pack_bf16x2(y[2], y[3]);
+        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * q4) = wv;
+      }
   }
 
   // Fixed maximum: every query tile of the wave in one pass over the keys.

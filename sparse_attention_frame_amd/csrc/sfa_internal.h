@@ -22,6 +22,28 @@ struct KeyRanges {
   int32_t r1_end;
 };
 
+// Key ranges of a set of frames made of the reference frame (if `ref`) and the
+// contiguous window frames [lo, hi] (none if lo > hi), in the form above: range 0
+// starts at token 0 (empty when the set lacks the reference frame), range 1 is the
+// rest.
+__host__ __device__ inline KeyRanges frame_set_ranges(bool ref, int lo, int hi, int T) {
+  KeyRanges r;
+  const bool win = lo <= hi;
+  if (ref && win && lo == 1) {
+    r.r0_end = (hi + 1) * T;
+    r.r1_begin = r.r1_end = r.r0_end;
+  } else if (ref) {
+    r.r0_end = T;
+    r.r1_begin = win ? lo * T : T;
+    r.r1_end = win ? (hi + 1) * T : T;
+  } else {
+    r.r0_end = 0;
+    r.r1_begin = lo * T;
+    r.r1_end = (hi + 1) * T;
+  }
+  return r;
+}
+
 __host__ __device__ inline KeyRanges key_ranges(int f, int F, int T, int w) {
   KeyRanges r;
   if (f == 0) {
@@ -52,8 +74,28 @@ __host__ __device__ inline int visible_frames(int f, int F, int w) {
   return 1 + (hi - lo + 1);
 }
 
+// Key split of a work item: the visible frames of query frame f (reference frame
+// first, then the window in order) cut into two halves, the first holding the
+// larger half. Each half is its own work item; the second of the two to finish adds
+// the other's partial output and row sum to its own (exact for a shared fixed
+// maximum, rescaled to the larger running maximum otherwise) and writes the result.
+__host__ __device__ inline KeyRanges half_key_ranges(int f, int half, int F, int T, int w) {
+  const int lo = f - w > 1 ? f - w : 1;
+  const int hi = f + w < F ? f + w : F;
+  const int n = 1 + (hi - lo + 1);  // visible frames: reference + window
+  const int na = (n + 1) / 2;       // frames of the first half (reference + na - 1 window)
+  if (half == 0) return frame_set_ranges(true, lo, lo + na - 2, T);
+  return frame_set_ranges(false, lo + na - 1, hi, T);
+}
+
+// Entries of the plan's frame order: the query frame in bits 0-9, the key half + 1
+// in bits 10-11 (0: whole item), the index of the split frame in bits 12-15.
+constexpr int kMaxSplitFrames = 16;
+
 struct Item {
   int32_t b, h, f, qb;
+  int32_t half;   // -1: all visible keys; 0 / 1: the first / second half of them
+  int32_t split;  // index of the split query frame (halves only)
 };
 
 // Item index -> work item. Groups of `nqb` items share one (frame, batch, head)
@@ -79,18 +121,26 @@ __host__ __device__ inline Item decode_item(int idx, const uint16_t* frame_order
   const int bh_count = B * H;
   const int fr = g / bh_count;
   const int bh = g - fr * bh_count;
+  const int e = frame_order[fr];
   Item it;
   it.b = bh / H;
   it.h = bh - it.b * H;
-  it.f = frame_order[fr];
+  it.f = e & 1023;
+  it.half = ((e >> 10) & 3) - 1;
+  it.split = e >> 12;
   it.qb = qb;
   return it;
 }
 
 struct Workspace {
   size_t mu, kmax, qmax, bound, elig, kvis, fbound, felig, qn, qmu, psum, pkmax, pqmax, vt,
-      queue, total;
+      queue, part, split_cnt, total;
 };
+
+// Partial result of one key half of a split item, in floats: O (not normalised) as
+// [wave][32-dim tile][register][lane] for 8 waves, then the row sum l and the
+// maximum m the partial is relative to, 256 rows each.
+__host__ __device__ constexpr int part_floats(int d) { return 8 * (d / 32) * 16 * 64 + 2 * 256; }
 
 // Work queue of the attention kernel in the workspace: one counter per XCD, a
 // count of workgroups that found no work left, padding to 64 bytes.
@@ -113,6 +163,8 @@ struct FwdParams {
   int32_t items;
   float c;        // scale * log2(e)
   int32_t* queue; // kQueueWords counters, zero between launches
+  float* part;        // [split item][half] partial results (part_floats(d) each)
+  int32_t* split_cnt; // [split item]: halves finished, zero between launches
   uint16_t frame_order[kMaxFrameSlots];
 };
 
@@ -136,6 +188,8 @@ struct NormParams {
   float* pkmax;   // [b][h][granule]: max ||k - mu||^2 over the 16 tokens of a granule
   float* pqmax;   // [b][h][granule]: max ||q||^2
   int32_t* queue; // the attention kernel's work queue, zeroed here
+  int32_t* split_cnt;  // the split items' counters, zeroed here
+  int32_t nsplit_cnt;
   int32_t B, H, S, D, nchunk;
   int32_t T, F, w;
   int32_t bound_mode;
@@ -211,6 +265,8 @@ struct sfa_plan {
   int32_t bound_mode;  // 0: per-head key-norm maximum; 1: per visible frame
   int32_t items;
   int32_t nchunk;   // norm-kernel token chunks
+  int32_t nslots;   // entries of frame_order: query frames, split ones twice
+  int32_t nsplit;   // query frames whose items are split into two key halves
   int64_t active_pairs;
   sfa::Workspace ws;
   uint16_t frame_order[sfa::kMaxFrameSlots];

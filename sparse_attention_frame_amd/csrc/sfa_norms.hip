@@ -186,6 +186,8 @@ __global__ __launch_bounds__(256) void final_kernel(NormParams p) {
   __shared__ float k2s[256], q2s[256];
   const int bh = blockIdx.x;
   if (bh == 0 && threadIdx.x < sfa::kQueueWords) p.queue[threadIdx.x] = 0;
+  // the split items' counters: block bh clears its share
+  for (int i = bh * 256 + threadIdx.x; i < p.nsplit_cnt; i += gridDim.x * 256) p.split_cnt[i] = 0;
   const int nf = p.F + 1;
   const int gpf = p.T / 16;  // granules per frame
   const int ngran = p.S / 16;

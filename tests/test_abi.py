@@ -60,8 +60,16 @@ def test_plan_tiles_divide_the_frame(L, name, block_q):
     assert p.info["block_q"] == block_q
     assert wl.tokens_per_frame % p.info["block_q"] == 0 and block_q % 16 == 0
     assert p.info["granule"] == 16
-    assert p.info["items"] == wl.batch * wl.heads * (wl.frames + 1) * (wl.tokens_per_frame //
-                                                                      block_q)
+    # the query frames seeing the fewest frames (more than one) run as two key halves
+    vis = [len(oracle.key_frames(f, wl.frames, wl.window)) for f in range(1, wl.frames + 1)]
+    vmin = min([v for v in vis if v >= 2], default=0)
+    assert p.info["split_frames"] == sum(v == vmin for v in vis)
+    assert p.info["items"] == wl.batch * wl.heads * (wl.frames + 1 + p.info["split_frames"]) * (
+        wl.tokens_per_frame // block_q)
+    off = Plan.for_workload(wl, key_split=-1)
+    assert off.info["split_frames"] == 0
+    assert off.info["items"] == wl.batch * wl.heads * (wl.frames + 1) * (wl.tokens_per_frame //
+                                                                        block_q)
 
 
 def test_active_pairs_match_oracle_and_golden(L):
@@ -99,16 +107,38 @@ def test_key_ranges_expand_to_the_oracle_mask(L, F, T, w):
 @pytest.mark.parametrize("B,H,F,T,w,bq", [(1, 12, 13, 3600, 2, 0), (2, 3, 4, 48, 1, 16),
                                           (1, 5, 7, 64, 3, 32), (3, 2, 0, 32, 0, 0),
                                           (1, 16, 13, 3600, 13, 0)])
-def test_work_items_cover_everything_once_largest_first(L, B, H, F, T, w, bq):
-    p = Plan(B, H, 128, F, T, w, block_q=bq)
+@pytest.mark.parametrize("key_split", [0, -1])
+def test_work_items_cover_everything_once_largest_first(L, B, H, F, T, w, bq, key_split):
+    """Every (batch, head, frame, query block) is covered exactly once: by one item that
+    sees all of the frame's keys, or by two key halves whose ranges are disjoint and
+    together give exactly those keys; items come largest first (cost = key frames)."""
+    p = Plan(B, H, 128, F, T, w, block_q=bq, key_split=key_split)
     n = p.info["items"]
     nqb = T // p.info["block_q"]
-    assert n == B * H * (F + 1) * nqb
+    nsplit = p.info["split_frames"]
+    assert n == B * H * (F + 1 + nsplit) * nqb
     items = [p.item(i) for i in range(n)]
-    assert len(set(items)) == n
-    for b, h, f, qb in items:
+    keys = [p.item_keys(i) for i in range(n)]
+    seen = {}
+    for (b, h, f, qb), (half, ranges) in zip(items, keys):
         assert 0 <= b < B and 0 <= h < H and 0 <= f <= F and 0 <= qb < nqb
-    cost = [len(oracle.key_frames(f, F, w)) for (_, _, f, _) in items]
+        seen.setdefault((b, h, f, qb), []).append((half, ranges))
+    assert len(seen) == B * H * (F + 1) * nqb
+    split_frames = set()
+    for (b, h, f, qb), parts in seen.items():
+        frames = np.zeros(F + 1, dtype=np.int32)   # key frames covered, with multiplicity
+        for half, ranges in parts:
+            for a, e in ranges:
+                assert a % T == 0 and e % T == 0 and a < e
+                frames[a // T:e // T] += 1
+        assert sorted(hf for hf, _ in parts) in ([-1], [0, 1])
+        if len(parts) == 2:
+            split_frames.add(f)
+        want = np.zeros(F + 1, dtype=np.int32)
+        want[oracle.key_frames(f, F, w)] = 1
+        np.testing.assert_array_equal(frames, want)
+    assert len(split_frames) == nsplit
+    cost = [sum(e - a for a, e in r) // T for (_, r) in keys]
     run = 8 * nqb
     full = n // run * run
     # whole runs of 8 groups: every run costs no more than the one before

@@ -139,7 +139,7 @@ def test_parity_sampled_d64_batch2_many_items(sfa, limit):
     q, k, v = to_dev(q_np, k_np, v_np)
     q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
     plan, out, ws = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit)
-    assert plan.info["items"] == B * H * (F + 1) * (T // 240)
+    assert plan.info["items"] == B * H * (F + 1 + plan.info["split_frames"]) * (T // 240)
     st, _ = check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
     assert st["eligible"].all() == (limit > 0)
     rows = np.array(sorted({f * T + r for f in range(F + 1) for r in (0, 239, 240, T - 1)}
@@ -388,11 +388,13 @@ OPTION_GEOMS = [(1, 8, 128, 8, 208, 2), (2, 2, 64, 6, 80, 1)]
 @pytest.mark.parametrize("geom_", OPTION_GEOMS)
 @pytest.mark.parametrize("opts", [dict(waves=8, lds_stages=2), dict(waves=8, lds_stages=4),
                                   dict(waves=4, lds_stages=2), dict(waves=4, lds_stages=3),
-                                  dict(waves=4, lds_stages=4), dict(block_q=16)])
+                                  dict(waves=4, lds_stages=4), dict(block_q=16),
+                                  dict(key_split=-1)])
 @pytest.mark.parametrize("limit", [40.0, -1.0])
 def test_plan_options_parity(sfa, geom_, opts, limit):
     """Every launch configuration sfa_plan_create_ex offers (4 waves of two query tiles, two
-    or four LDS stages, one-granule query blocks), both softmax paths, against the oracle."""
+    or four LDS stages, one-granule query blocks, no key split), both softmax paths, against
+    the oracle."""
     B, H, d, F, T, w = geom_
     say(f"[plan_options] {geom_} {opts} limit={limit}")
     S = (F + 1) * T
@@ -449,3 +451,35 @@ def test_random_geometries_and_options(sfa, F, T, w, H, d, B, waves, stages, lim
     ref = oracle.attention(q_np, k_np, v_np, F, T, w)
     assert_close(out.float().cpu().numpy(), ref, "random")
     check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
+
+
+@pytest.mark.parametrize("limit", [40.0, -1.0])
+def test_key_split_halves_merge(sfa, limit):
+    """The items of the cheapest multi-frame query frames run as two key halves merged by
+    whichever finishes second: both paths match the oracle, the merged rows agree with the
+    unsplit run to rounding, rows of the other frames are bitwise those of the unsplit run,
+    and two runs are bitwise identical whatever the finishing order."""
+    F, T, w, H, d, B = 9, 240, 2, 4, 128, 2
+    say(f"[key_split] limit={limit}")
+    S = (F + 1) * T
+    g = np.random.default_rng(91)
+    q_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    k_np = (g.standard_normal((B, S, H, d)) + 3 * g.standard_normal((B, 1, H, d))).astype(
+        np.float32)
+    v_np = g.standard_normal((B, S, H, d)).astype(np.float32)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
+    plan, a, _ = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit)
+    assert plan.info["split_frames"] == 2        # frames 1 and F see 4 frames, the fewest
+    _, b, _ = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit)
+    assert torch.equal(a, b)
+    _, whole, _ = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit, key_split=-1)
+    ref = oracle.attention(q_np, k_np, v_np, F, T, w)
+    assert_close(a.float().cpu().numpy(), ref, "split")
+    assert_close(whole.float().cpu().numpy(), ref, "whole")
+    split_rows = torch.zeros(S, dtype=torch.bool)
+    split_rows[T:2 * T] = True
+    split_rows[F * T:] = True
+    assert torch.equal(a[:, ~split_rows.cuda()], whole[:, ~split_rows.cuda()])
+    diff = (a[:, split_rows.cuda()].float() - whole[:, split_rows.cuda()].float()).abs().max()
+    assert float(diff) <= 2e-2
