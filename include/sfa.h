@@ -160,7 +160,10 @@ int sfa_norms(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, vo
  * may not alias q, k or v. The launch is persistent (at most one workgroup per
  * CU) and takes its work items from counters in the workspace, which sfa_norms
  * zeroes and every launch leaves at zero: sfa_fwd may run any number of times
- * after one sfa_norms, but two calls in flight at once on one workspace race. */
+ * after one sfa_norms, but two calls in flight at once on one workspace race.
+ * The key halves of split items (sfa_plan_options.key_split) meet through partial
+ * results and counters in the same workspace; the output does not depend on which
+ * half finishes first. */
 int sfa_fwd(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_tensor o,
             void* workspace, size_t workspace_bytes, void* stream);
 
