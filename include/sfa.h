@@ -69,10 +69,12 @@ typedef struct sfa_tensor {
 typedef struct sfa_plan sfa_plan;
 
 typedef struct sfa_plan_info {
-  int32_t block_q;          /* query rows per work item; divides T, multiple of 16 */
+  int32_t block_q;          /* query rows per work item, a multiple of 16; the last item
+                               of each frame holds the T mod block_q rows left, if any */
   int32_t granule;          /* token granule of the key loop (16) */
   int32_t waves_per_item;   /* 64-lane waves in one workgroup */
-  int32_t items;            /* work items = B * H * (F + 1 + split_frames) * (T / block_q) */
+  int32_t items;            /* work items = B * H * (F + 1 + split_frames) *
+                               ceil(T / block_q) */
   int64_t active_pairs;     /* visible (query, key) pairs summed over B and H */
   double active_flops;      /* 4 * d * active_pairs (q.k and p.v, 2 flops per MAC) */
   int64_t io_bytes;         /* q, k, v read once and o written once: 8 * B * S * H * d */
@@ -88,8 +90,9 @@ int sfa_plan_create(const sfa_geometry* geom, sfa_plan** out);
 
 /* Tuning overrides for sfa_plan_create_ex; 0 in a field selects the default. */
 typedef struct sfa_plan_options {
-  int32_t block_q;        /* query rows per work item: a multiple of 16 that divides T,
-                             at most 256 (default: the largest such divisor) */
+  int32_t block_q;        /* query rows per work item: a multiple of 16, at most 256,
+                             cut to T (default: min(T, 256)); when it does not divide
+                             T, the last item of each frame takes the rows left */
   int32_t waves_per_item; /* 8 (default: 32 query rows per wave, two waves per SIMD)
                              or 4 (64 rows per wave, one wave per SIMD) */
   int32_t lds_stages;     /* 64-key K/V stages in LDS: 2, 3 or 4 (default 3, which

@@ -47,12 +47,13 @@ int validate_geometry(const sfa_geometry* g) {
   return SFA_OK;
 }
 
-// Query granules per work item: the largest divisor of T/16 that fits one
-// workgroup (8 query tiles of 32 rows).
+// Query granules per work item: as many as one workgroup holds (8 query tiles of
+// 32 rows), or the whole frame when it is shorter. The last block of a frame takes
+// the remaining rows, so a frame costs ceil(T / 32) wave tiles, the fewest possible
+// (a block size that divides T, such as 240 rows for T = 3600, leaves 16 repeated
+// rows in the last wave tile of every block).
 int auto_block_granules(int t_granules) {
-  for (int g = kMaxBlockGranules; g >= 1; --g)
-    if (t_granules % g == 0) return g;
-  return 1;
+  return t_granules < kMaxBlockGranules ? t_granules : kMaxBlockGranules;
 }
 
 int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out) {
@@ -75,10 +76,10 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   if (block_q == 0) {
     gq = auto_block_granules(tg);
   } else {
-    if (block_q < 0 || block_q % kGranule != 0 || T % block_q != 0 ||
-        block_q / kGranule > kMaxBlockGranules)
+    if (block_q < 0 || block_q % kGranule != 0 || block_q / kGranule > kMaxBlockGranules)
       return SFA_ERR_UNSUPPORTED;
     gq = block_q / kGranule;
+    if (gq > tg) gq = tg;  // one block holds the whole frame
   }
   sfa_plan* p = new (std::nothrow) sfa_plan;
   if (!p) return SFA_ERR_NOMEM;
@@ -92,7 +93,7 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   p->waves = waves;
   p->stages = stages;
   p->bound_mode = bound_mode;
-  p->nqb = tg / gq;
+  p->nqb = (tg + gq - 1) / gq;  // the last block of a frame may be shorter
   p->nchunk = (p->S + kNormChunk - 1) / kNormChunk;
 
   // Key split of the tail: the items of the cheapest query frames that see more than

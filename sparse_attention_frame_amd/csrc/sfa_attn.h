@@ -21,12 +21,13 @@
 //   * section "Proving pixels unchanged": P is rounded to bf16 and PV runs on
 //     the bf16 matrix cores with fp32 accumulation.
 //
-// Work decomposition: a work item is one query block of 16*gq rows (gq | T/16)
-// of one (batch, head, frame); a workgroup runs one item at a time (the attention
-// kernel keeps its workgroups resident and hands them items from a queue). WAVES
-// waves each own QT 32-row query tiles; when gq is odd the last tile holds 16 real
-// rows and 16 repeats that are computed but never stored. All waves stream the same
-// key granules through LDS.
+// Work decomposition: a work item is one query block of 16*gq rows of one (batch,
+// head, frame), the last block of a frame whatever rows are left (a multiple of 16);
+// a workgroup runs one item at a time (the attention kernel keeps its workgroups
+// resident and hands them items from a queue). WAVES waves each own QT 32-row query
+// tiles; a tile with 16 real rows holds 16 repeats that are computed but never
+// stored, and a wave with no real row only helps move the keys. All waves stream the
+// same key granules through LDS.
 //
 // MFMA orientation (v_mfma_f32_32x32x16_bf16, wave64; 32x32x16 runs at twice
 // the rate of 16x16x32 on this chip):
@@ -450,12 +451,12 @@ struct Attn {
     const char* vtb =
         reinterpret_cast<const char*>(p.vt + (int64_t(it.b) * p.H + it.h) * D * p.S);
 
-    const int rows = p.gq * 16;                 // real rows of this item
-    const int row0 = it.f * p.T + it.qb * rows;
+    const int rows = min(p.gq * 16, p.T - it.qb * p.gq * 16);  // real rows of this item
+    const int row0 = it.f * p.T + it.qb * p.gq * 16;
     const int64_t rowstat = (int64_t(it.b) * p.H + it.h) * p.S;
     const float kmax = p.kvis[(int64_t(it.b) * p.H + it.h) * (p.F + 1) + it.f];
-    // a wave whose query tiles hold no real row only helps with the DMA
-    const bool active = (wave * QT + t0) * 32 < rows;
+    // a wave whose query tiles hold no real row only helps with the DMA (wave-uniform)
+    const bool active = __builtin_amdgcn_readfirstlane((wave * QT + t0) * 32) < rows;
 
     Lane L;
     Slots W;
@@ -506,6 +507,17 @@ struct Attn {
         wait_vm<0>();
         __syncthreads();
         if (1 < nst) issue_stage(lds, 1, L, W, X, 1, 1 < nfull ? 4 : rem);
+      }
+      if (N > 0 && !active) {
+        // no real row: the same DMA issues and barriers as the regions below, no compute
+        for (int j = 1; j < N - 1; j += 2) {
+          const int sn = (j + 1) / 2;
+          wait_vm<0>();
+          __syncthreads();
+          if (sn + 1 < nst)
+            issue_stage(lds, (sn + 1) % 3, L, W, X, sn + 1, sn + 1 < nfull ? 4 : rem);
+        }
+      } else if (N > 0) {
         KFrag kf;
         VFrag vf;
         uint32_t pprev[8], pcur[8];
@@ -563,11 +575,13 @@ struct Attn {
         wait_vm<0>();
         __syncthreads();
         const int kl = (nfull % NBUF) * STAGE_B;
-        if (rem >= 2)
+        if (!active) {
+        } else if (rem >= 2) {
           tile<false, ONLINE, NT>(lds, L, kl, kl, qf, o, mrow, lsum, p.c);
-        else
+        } else {
           tile<true, ONLINE, NT>(lds, L, kl, kl, qf, o, mrow, lsum, p.c);
-        if (rem == 3)
+        }
+        if (active && rem == 3)
           tile<true, ONLINE, NT>(lds, L, kl + 32 * ROWB, kl + 2 * VG_B, qf, o, mrow, lsum, p.c);
       }
     } else {

@@ -158,8 +158,8 @@ struct FwdParams {
   const uint8_t* felig;  // [b][h][F+1]: the items of the query frame take the fixed maximum
   const uint16_t* vt;  // V^T staged by the prologue: [b][h][d][S]
   int32_t B, H, S, T, F, w;
-  int32_t gq;     // query granules per item
-  int32_t nqb;    // items per (frame, batch, head)
+  int32_t gq;     // query granules per item (the last item of a frame: what is left)
+  int32_t nqb;    // items per (frame, batch, head): ceil(T / (16 * gq))
   int32_t items;
   float c;        // scale * log2(e)
   int32_t* queue; // kQueueWords counters, zero between launches
@@ -261,7 +261,7 @@ struct sfa_plan {
   int32_t gq;       // query granules per item (block_q / 16)
   int32_t waves;    // waves per attention workgroup (4 or 8)
   int32_t stages;   // 64-key LDS stages in flight (2..4)
-  int32_t nqb;      // T / block_q
+  int32_t nqb;      // ceil(T / block_q)
   int32_t bound_mode;  // 0: per-head key-norm maximum; 1: per visible frame
   int32_t items;
   int32_t nchunk;   // norm-kernel token chunks

@@ -1,7 +1,7 @@
 """C-ABI checks that need no GPU: exports, planning, work order and argument errors.
 
 Planning follows "HeyGen x Google Cloud: Bringing Avatar IV to TPUs", section
-"Deleting the mask": query blocks divide the frame span, key ranges are whole
+"Deleting the mask": query blocks lie inside one frame, key ranges are whole
 frames (reference + window), so the plan's ranges expanded to tokens must
 equal the oracle's mask exactly.
 """
@@ -52,24 +52,25 @@ def test_status_strings(L):
     assert b"unknown" in L.sfa_status_str(7)
 
 
-@pytest.mark.parametrize("name,block_q", [("tiny", 48), ("small", 208), ("720p", 240),
-                                          ("1080p", 240), ("stress", 240)])
-def test_plan_tiles_divide_the_frame(L, name, block_q):
+@pytest.mark.parametrize("name,block_q", [("tiny", 48), ("small", 208), ("720p", 256),
+                                          ("1080p", 256), ("stress", 256)])
+def test_plan_query_blocks_cover_the_frame(L, name, block_q):
     wl = W.ALL[name]
     p = Plan.for_workload(wl)
-    assert p.info["block_q"] == block_q
-    assert wl.tokens_per_frame % p.info["block_q"] == 0 and block_q % 16 == 0
+    T = wl.tokens_per_frame
+    nqb = -(-T // block_q)
+    assert p.info["block_q"] == block_q and block_q % 16 == 0
+    # blocks of block_q rows, the last one ragged: a frame costs ceil(T / 32) wave tiles
+    assert (nqb - 1) * block_q < T <= nqb * block_q
     assert p.info["granule"] == 16
     # the query frames seeing the fewest frames (more than one) run as two key halves
     vis = [len(oracle.key_frames(f, wl.frames, wl.window)) for f in range(1, wl.frames + 1)]
     vmin = min([v for v in vis if v >= 2], default=0)
     assert p.info["split_frames"] == sum(v == vmin for v in vis)
-    assert p.info["items"] == wl.batch * wl.heads * (wl.frames + 1 + p.info["split_frames"]) * (
-        wl.tokens_per_frame // block_q)
+    assert p.info["items"] == wl.batch * wl.heads * (wl.frames + 1 + p.info["split_frames"]) * nqb
     off = Plan.for_workload(wl, key_split=-1)
     assert off.info["split_frames"] == 0
-    assert off.info["items"] == wl.batch * wl.heads * (wl.frames + 1) * (wl.tokens_per_frame //
-                                                                        block_q)
+    assert off.info["items"] == wl.batch * wl.heads * (wl.frames + 1) * nqb
 
 
 def test_active_pairs_match_oracle_and_golden(L):
@@ -106,7 +107,8 @@ def test_key_ranges_expand_to_the_oracle_mask(L, F, T, w):
 
 @pytest.mark.parametrize("B,H,F,T,w,bq", [(1, 12, 13, 3600, 2, 0), (2, 3, 4, 48, 1, 16),
                                           (1, 5, 7, 64, 3, 32), (3, 2, 0, 32, 0, 0),
-                                          (1, 16, 13, 3600, 13, 0)])
+                                          (1, 16, 13, 3600, 13, 0), (2, 2, 5, 208, 1, 112),
+                                          (1, 3, 3, 48, 2, 32)])
 @pytest.mark.parametrize("key_split", [0, -1])
 def test_work_items_cover_everything_once_largest_first(L, B, H, F, T, w, bq, key_split):
     """Every (batch, head, frame, query block) is covered exactly once: by one item that
@@ -114,7 +116,7 @@ def test_work_items_cover_everything_once_largest_first(L, B, H, F, T, w, bq, ke
     together give exactly those keys; items come largest first (cost = key frames)."""
     p = Plan(B, H, 128, F, T, w, block_q=bq, key_split=key_split)
     n = p.info["items"]
-    nqb = T // p.info["block_q"]
+    nqb = -(-T // p.info["block_q"])
     nsplit = p.info["split_frames"]
     assert n == B * H * (F + 1 + nsplit) * nqb
     items = [p.item(i) for i in range(n)]
@@ -187,10 +189,17 @@ def test_largest_frame_count_is_accepted(L):
 def test_tile_override_errors(L):
     h = ctypes.c_void_p()
     g = _geom()
-    for bq in (8, 32, 96, 272, -16):     # not a multiple of 16, not dividing 48, too large
+    for bq in (8, 24, 272, -16):     # not a multiple of 16, too large, negative
         opt = _lib.PlanOptions(bq, 0, 0)
         assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == \
             _lib.SFA_ERR_UNSUPPORTED, bq
+    for bq, want in ((32, 32), (96, 48), (256, 48)):   # ragged last block; at most the frame
+        opt = _lib.PlanOptions(bq, 0, 0)
+        assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == 0
+        info = _lib.PlanInfo()
+        assert L.sfa_plan_get_info(h, ctypes.byref(info)) == 0
+        assert info.block_q == want, bq
+        L.sfa_plan_destroy(h)
     for waves in (1, 2, 6, 16, -4):
         opt = _lib.PlanOptions(0, waves, 0)
         assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == \

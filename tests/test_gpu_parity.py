@@ -96,7 +96,10 @@ def sample_rows(wl, n_random=24, seed=0):
     T, S = wl.tokens_per_frame, wl.seq
     rows = set()
     for f in range(wl.frames + 1):
-        rows.update({f * T, f * T + 15, f * T + 16, f * T + T // 2, (f + 1) * T - 1})
+        # frame edges, granule and 256-row block edges, the ragged last block of the frame
+        rows.update({f * T, f * T + 15, f * T + 16, f * T + 255, f * T + 256, f * T + T // 2,
+                     f * T + (T - 1) // 256 * 256 - 1, f * T + (T - 1) // 256 * 256,
+                     (f + 1) * T - 17, (f + 1) * T - 16, (f + 1) * T - 1})
     g = np.random.default_rng(seed)
     rows.update(int(x) for x in g.integers(0, S, n_random))
     return np.array(sorted(rows))
@@ -139,10 +142,12 @@ def test_parity_sampled_d64_batch2_many_items(sfa, limit):
     q, k, v = to_dev(q_np, k_np, v_np)
     q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
     plan, out, ws = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit)
-    assert plan.info["items"] == B * H * (F + 1 + plan.info["split_frames"]) * (T // 240)
+    # 256-row query blocks: 256, 256 and a ragged 208 per frame
+    assert plan.info["items"] == B * H * (F + 1 + plan.info["split_frames"]) * 3
     st, _ = check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
     assert st["eligible"].all() == (limit > 0)
-    rows = np.array(sorted({f * T + r for f in range(F + 1) for r in (0, 239, 240, T - 1)}
+    rows = np.array(sorted({f * T + r for f in range(F + 1)
+                            for r in (0, 255, 256, 511, 512, 687, 688, T - 1)}
                            | set(g.integers(0, S, 16).tolist())))
     got_all = out[:, torch.from_numpy(rows).cuda()].float().cpu().numpy()   # [B, R, H, d]
     for b in range(B):
@@ -389,12 +394,15 @@ OPTION_GEOMS = [(1, 8, 128, 8, 208, 2), (2, 2, 64, 6, 80, 1)]
 @pytest.mark.parametrize("opts", [dict(waves=8, lds_stages=2), dict(waves=8, lds_stages=4),
                                   dict(waves=4, lds_stages=2), dict(waves=4, lds_stages=3),
                                   dict(waves=4, lds_stages=4), dict(block_q=16),
+                                  dict(block_q=48), dict(block_q=48, waves=4),
+                                  dict(block_q=112), dict(block_q=112, lds_stages=2),
                                   dict(key_split=-1)])
 @pytest.mark.parametrize("limit", [40.0, -1.0])
 def test_plan_options_parity(sfa, geom_, opts, limit):
     """Every launch configuration sfa_plan_create_ex offers (4 waves of two query tiles, two
-    or four LDS stages, one-granule query blocks, no key split), both softmax paths, against
-    the oracle."""
+    or four LDS stages, one-granule query blocks, query blocks that do not divide the frame
+    so that its last block is ragged and some waves hold no real row, no key split), both
+    softmax paths, against the oracle."""
     B, H, d, F, T, w = geom_
     say(f"[plan_options] {geom_} {opts} limit={limit}")
     S = (F + 1) * T
@@ -407,7 +415,7 @@ def test_plan_options_parity(sfa, geom_, opts, limit):
     q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
     plan, out, ws = run(sfa, geom_, q, k, v, bound_limit=limit, **opts)
     if "block_q" in opts:
-        assert plan.info["block_q"] == opts["block_q"]
+        assert plan.info["block_q"] == min(opts["block_q"], T)
     if "waves" in opts:
         assert plan.info["waves_per_item"] == opts["waves"]
     ref = oracle.attention(q_np, k_np, v_np, F, T, w)
