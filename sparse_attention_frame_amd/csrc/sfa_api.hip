@@ -1,9 +1,10 @@
 // C ABI: planning (host only), argument validation and kernel launches.
 //
 // Planning follows "HeyGen x Google Cloud: Bringing Avatar IV to TPUs",
-// section "Deleting the mask": query blocks are whole 16-token granules that
-// divide the frame span T, so every (query block, key granule) pair is either
-// fully visible or skipped and the key loop never needs a mask or padding.
+// section "Deleting the mask": query blocks are whole 16-token granules inside
+// one frame (the frame span T is a multiple of 16), so every (query block, key
+// granule) pair is either fully visible or skipped and the key loop never needs
+// a mask or padding.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
