@@ -95,8 +95,9 @@ typedef struct sfa_plan_options {
                              T, the last item of each frame takes the rows left */
   int32_t waves_per_item; /* 8 (default: 32 query rows per wave, two waves per SIMD)
                              or 4 (64 rows per wave, one wave per SIMD) */
-  int32_t lds_stages;     /* 64-key K/V stages in LDS: 2, 3 or 4 (default 3, which
-                             selects the software-pipelined loop of the 8-wave kernel) */
+  int32_t lds_stages;     /* 64-key K/V stages in LDS: 2, 3 or 4 (default 3; 3 and 4
+                             select the software-pipelined loop of the 8-wave kernel,
+                             with 1 or 2 stages in flight while one is read) */
   int32_t bound_mode;     /* how the fixed maximum is bounded (section "Unchaining
                              softmax": query norm times the largest mean-centred key norm):
                              0 (default) per (b, h): the largest key norm of the head, one

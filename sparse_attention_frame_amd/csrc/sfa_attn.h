@@ -491,31 +491,43 @@ struct Attn {
     const int nfull = ngran / 4;
     const int rem = ngran - nfull * 4;
     const int nst = nfull + (rem > 0 ? 1 : 0);
-    if constexpr (!ONLINE && NT == 1 && NBUF == 3) {
+    if constexpr (!ONLINE && NT == 1 && (NBUF == 3 || NBUF == 4)) {
       // Tile-level software pipeline over the N = 2*nfull full 32-key tiles:
       //   region j:  QK(j+1) + PV(j-1)  (16 MFMAs)  ||  softmax(j)  (48 VALU)
       // Region j reads K(j+1) for its own QK and V^T(j) for the PV of region j+1,
       // so the V^T reads have a whole region to land. Stage s (tiles 2s, 2s+1)
-      // sits in buffer s % 3; barrier B_s, just before the region that first
-      // reads stage s, waits for its DMA and then launches the DMA of stage s + 1
-      // into the buffer of stage s - 2, whose last read (V^T of tile 2s - 3, in
-      // region 2s - 3) was consumed by the PV of region 2s - 2, before B_s.
+      // sits in buffer s % NBUF; barrier B_s, just before the region that first
+      // reads stage s, waits for its DMA and then launches the DMA of stage
+      // s + NBUF - 2 into the buffer of stage s - 2, whose last read (V^T of tile
+      // 2s - 3, in region 2s - 3) was consumed by the PV of region 2s - 2, before B_s.
+      // So NBUF - 2 stages are in flight while one is read.
+      constexpr int AH = NBUF - 2;
+      // wait for stage sn's DMA: with AH == 2 the next stage's (DMA_W per wave when it is
+      // a full stage) may stay in flight
+      auto wait_stage = [&](int sn) {
+        if (AH == 2 && sn + 1 < nfull)
+          wait_vm<(AH - 1) * DMA_W>();
+        else
+          wait_vm<0>();
+      };
       const int N = 2 * nfull;
       f32x16(&oo)[DT] = o[0];
       if (N > 0) {
         issue_stage(lds, 0, L, W, X, 0, 4);
         wait_vm<0>();
         __syncthreads();
-        if (1 < nst) issue_stage(lds, 1, L, W, X, 1, 1 < nfull ? 4 : rem);
+#pragma unroll
+        for (int a = 1; a <= AH; ++a)
+          if (a < nst) issue_stage(lds, a, L, W, X, a, a < nfull ? 4 : rem);
       }
       if (N > 0 && !active) {
         // no real row: the same DMA issues and barriers as the regions below, no compute
         for (int j = 1; j < N - 1; j += 2) {
           const int sn = (j + 1) / 2;
-          wait_vm<0>();
+          wait_stage(sn);
           __syncthreads();
-          if (sn + 1 < nst)
-            issue_stage(lds, (sn + 1) % 3, L, W, X, sn + 1, sn + 1 < nfull ? 4 : rem);
+          if (sn + AH < nst)
+            issue_stage(lds, (sn + AH) % NBUF, L, W, X, sn + AH, sn + AH < nfull ? 4 : rem);
         }
       } else if (N > 0) {
         KFrag kf;
@@ -531,21 +543,22 @@ struct Attn {
         softmax_fixed(scur, mrow[0], lsum[0], pprev, p.c);
         scur = snext;
         __builtin_amdgcn_sched_barrier(0);
-        // steady regions j = 1 .. N-2, unrolled over the 6-tile period of (buffer, half)
-        for (int j0 = 1; j0 < N - 1; j0 += 6) {
+        // steady regions j = 1 .. N-2, unrolled over the 2*NBUF-tile period of (buffer, half)
+        for (int j0 = 1; j0 < N - 1; j0 += 2 * NBUF) {
 #pragma unroll
-          for (int u = 0; u < 6; ++u) {
+          for (int u = 0; u < 2 * NBUF; ++u) {
             const int j = j0 + u;
             if (j >= N - 1) break;
             if ((u & 1) == 0) {  // j odd: tile j+1 opens stage (j+1)/2
               const int sn = (j + 1) / 2;
-              wait_vm<0>();
+              wait_stage(sn);
               __syncthreads();
-              if (sn + 1 < nst)
-                issue_stage(lds, (sn + 1) % 3, L, W, X, sn + 1, sn + 1 < nfull ? 4 : rem);
+              if (sn + AH < nst)
+                issue_stage(lds, (sn + AH) % NBUF, L, W, X, sn + AH, sn + AH < nfull ? 4 : rem);
             }
-            const int bn = ((u + 2) / 2) % 3, tn = (u + 2) & 1;  // tile j+1 = 1 + u + 1 (mod 6)
-            const int bc = ((u + 1) / 2) % 3, tc = (u + 1) & 1;  // tile j = 1 + u (mod 6)
+            // tile j+1 = 1 + u + 1 and tile j = 1 + u (mod 2*NBUF)
+            const int bn = ((u + 2) / 2) % NBUF, tn = (u + 2) & 1;
+            const int bc = ((u + 1) / 2) % NBUF, tc = (u + 1) & 1;
             __builtin_amdgcn_sched_barrier(0);
             load_k(kf, lds, L, bn * STAGE_B + tn * 32 * ROWB);
             snext = qk(kf, qf[0]);
@@ -562,7 +575,7 @@ struct Attn {
         // region N-1: PV(N-2) + softmax(N-1); then PV(N-1)
         {
           const int jm = N - 2;  // tiles N-2 and N-1 are the two halves of stage nfull-1
-          const int b = ((jm / 2) % 3);
+          const int b = ((jm / 2) % NBUF);
           pv(vf, pprev, oo);     // V^T(N-2), read in region N-2
           softmax_fixed(scur, mrow[0], lsum[0], pcur, p.c);
           load_v(vf, lds, L, b * STAGE_B + 2 * VG_B);
