@@ -396,6 +396,7 @@ OPTION_GEOMS = [(1, 8, 128, 8, 208, 2), (2, 2, 64, 6, 80, 1)]
                                   dict(waves=4, lds_stages=4), dict(block_q=16),
                                   dict(block_q=48), dict(block_q=48, waves=4),
                                   dict(block_q=112), dict(block_q=112, lds_stages=2),
+                                  dict(block_q=48, lds_stages=4),
                                   dict(key_split=-1)])
 @pytest.mark.parametrize("limit", [40.0, -1.0])
 def test_plan_options_parity(sfa, geom_, opts, limit):
