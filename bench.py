@@ -262,6 +262,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--waves", type=int, default=0, help="override waves per workgroup (4 or 8)")
     ap.add_argument("--block-q", type=int, default=0, help="override query rows per work item")
+    ap.add_argument("--wave-rows", type=int, default=0,
+                    help="override query rows per wave (32 or 64 with 8 waves)")
     ap.add_argument("--lds-stages", type=int, default=0, help="override K/V stages in flight")
     ap.add_argument("--key-split", type=int, default=0, choices=(0, -1),
                     help="0: the plan splits the tail items into two key halves; -1: never")
@@ -303,7 +305,8 @@ def main():
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q_np, k_np, v_np))
     plan = sfa.Plan.for_workload(wl, waves=args.waves, block_q=args.block_q,
                                  lds_stages=args.lds_stages, bound_mode=args.bound_mode,
-                                 bound_limit=args.bound_limit, key_split=args.key_split)
+                                 bound_limit=args.bound_limit, key_split=args.key_split,
+                                 wave_rows=args.wave_rows)
     ws = plan.workspace(dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
@@ -315,7 +318,8 @@ def main():
         gplan = sfa.Plan(wl.batch, wl.heads // G, wl.head_dim, wl.frames, wl.tokens_per_frame,
                          wl.window, waves=args.waves, block_q=args.block_q,
                          lds_stages=args.lds_stages, bound_mode=args.bound_mode,
-                         bound_limit=args.bound_limit, key_split=args.key_split)
+                         bound_limit=args.bound_limit, key_split=args.key_split,
+                         wave_rows=args.wave_rows)
         gws = torch.empty(G * gplan.info["workspace_bytes"], dtype=torch.uint8, device=dev)
         gstreams = [torch.cuda.Stream() for _ in range(args.group_streams)]
 
@@ -391,6 +395,7 @@ def main():
                                f"T={wl.tokens_per_frame} tokens (S={wl.seq}), H={wl.heads}, "
                                f"d={wl.head_dim}, window +-{wl.window}, batch {wl.batch}",
                    "block_q": info["block_q"], "waves": info["waves_per_item"],
+                   "wave_rows": info["wave_rows"],
                    "items": info["items"], "split_frames": info["split_frames"],
                    "active_gflop": round(flops / 1e9, 1),
                    "eligible_heads": int(st["eligible"].sum()), "heads": wl.heads,
@@ -413,7 +418,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": (traffic if G == 1 and args.bound_mode == 0
                                  and wl.name == "720p" and args.bound_limit == 40.0
-                                 and not (args.waves or args.block_q or args.lds_stages or args.key_split)
+                                 and not (args.waves or args.block_q or args.lds_stages or args.key_split
+                                          or args.wave_rows)
                                  and args.ablation == "none" else None)},
     }
     if args.copy_probe_mib:

@@ -82,6 +82,7 @@ typedef struct sfa_plan_info {
   int32_t bound_mode;       /* the plan's bound_mode (see sfa_plan_options) */
   int32_t split_frames;     /* query frames whose work items run as two key halves (see
                                sfa_plan_options.key_split) */
+  int32_t wave_rows;        /* query rows per wave (32 or 64) */
 } sfa_plan_info;
 
 /* Validates the geometry and builds the work decomposition (host only, no HIP
@@ -90,14 +91,17 @@ int sfa_plan_create(const sfa_geometry* geom, sfa_plan** out);
 
 /* Tuning overrides for sfa_plan_create_ex; 0 in a field selects the default. */
 typedef struct sfa_plan_options {
-  int32_t block_q;        /* query rows per work item: a multiple of 16, at most 256,
-                             cut to T (default: min(T, 256)); when it does not divide
-                             T, the last item of each frame takes the rows left */
-  int32_t waves_per_item; /* 8 (default: 32 query rows per wave, two waves per SIMD)
-                             or 4 (64 rows per wave, one wave per SIMD) */
-  int32_t lds_stages;     /* 64-key K/V stages in LDS: 2, 3 or 4 (default 3; 3 and 4
-                             select the software-pipelined loop of the 8-wave kernel,
-                             with 1 or 2 stages in flight while one is read) */
+  int32_t block_q;        /* query rows per work item: a multiple of 16, at most
+                             waves_per_item * wave_rows, cut to T (default: that maximum,
+                             or less when the launch would otherwise have fewer work items
+                             than 256 compute units); when it does not divide T, the last
+                             item of each frame takes the rows left */
+  int32_t waves_per_item; /* 8 (default: two waves per SIMD), 12 (three per SIMD, 32 query
+                             rows each, 96-key LDS stages) or 4 (one wave per SIMD, 512
+                             registers, 64 query rows per wave) */
+  int32_t lds_stages;     /* K/V stages in LDS: 2, 3 or 4 (2 or 3 with 12 waves; default 3).
+                             With 8 waves of 32 rows, 3 and 4 select the software-pipelined
+                             loop, with 1 or 2 stages in flight while one is read */
   int32_t bound_mode;     /* how the fixed maximum is bounded (section "Unchaining
                              softmax": query norm times the largest mean-centred key norm):
                              0 (default) per (b, h): the largest key norm of the head, one
@@ -113,6 +117,12 @@ typedef struct sfa_plan_options {
                              fixed maximum the halves simply add); they are the last long
                              items of the largest-first order, so the launch's tail gets
                              shorter. -1: never split. */
+  int32_t wave_rows;      /* query rows per wave with 8 waves: 32 (default: one 32-row
+                             query tile, 256-row work items, software-pipelined loop) or 64
+                             (two tiles, so every K or V^T operand read from LDS feeds two
+                             MFMAs; 512-row items; measured slower on MI355X: the 256
+                             registers of a wave leave no room to overlap its softmax with
+                             its MFMAs). 4 waves: 64 only; 12 waves: 32 only. */
 } sfa_plan_options;
 
 /* sfa_plan_create with overrides (options may be NULL). Values outside the
@@ -149,19 +159,22 @@ int sfa_plan_item_keys(const sfa_plan* plan, int32_t index, int32_t* half, int32
  *    (b, h) the key mean mu, max_j ||k_j - mu||, max_i ||q_i||, the bound and
  *    the eligibility flag; per (b, h, query frame) the key-norm maximum, bound
  *    and flag the plan's bound_mode selects; per row ||q_i|| and <q_i, mu>
- *    (fp32; q read once, k twice; fixed reduction order, no atomics, so
- *    bit-deterministic);
- *  - V^T [b][h][d][S] in bf16, the layout the attention kernel reads.
+ *    (fp32; q read once, k three times, v once; fixed reduction order, no
+ *    atomics, so bit-deterministic);
+ *  - k and v staged in bf16 in the layout of the attention kernel's LDS stages
+ *    (per (b, h), 16-token granules of 32 * d bytes: k as [granule][8-element
+ *    chunk][16 keys][8], v as [granule][d][16 keys] with the two 8-key halves of
+ *    each row swapped when (d / 8) is odd), see sfa_read_staged.
  * Must run on the current q, k and v before sfa_fwd. */
 int sfa_norms(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, void* workspace,
               size_t workspace_bytes, void* stream);
 
 /* The attention kernel (one launch): one pass over each query block's
  * reference-frame and window key granules, with the fixed maximum for eligible
- * heads and the online softmax for the others. Reads q and k from their
- * tensors and V^T from the workspace, so sfa_norms must have run on the same
- * q, k, v and workspace earlier on the stream; v itself is only validated. o
- * may not alias q, k or v. The launch is persistent (at most one workgroup per
+ * heads and the online softmax for the others. Reads q from its tensor and the
+ * staged copies of k and v from the workspace, so sfa_norms must have run on the
+ * same q, k, v and workspace earlier on the stream; k and v themselves are only
+ * validated. o may not alias q, k or v. The launch is persistent (at most one workgroup per
  * CU) and takes its work items from counters in the workspace, which sfa_norms
  * zeroes and every launch leaves at zero: sfa_fwd may run any number of times
  * after one sfa_norms, but two calls in flight at once on one workspace race.

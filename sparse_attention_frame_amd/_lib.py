@@ -29,7 +29,7 @@ class Tensor(ctypes.Structure):
 class PlanOptions(ctypes.Structure):
     _fields_ = [("block_q", ctypes.c_int32), ("waves_per_item", ctypes.c_int32),
                 ("lds_stages", ctypes.c_int32), ("bound_mode", ctypes.c_int32),
-                ("key_split", ctypes.c_int32)]
+                ("key_split", ctypes.c_int32), ("wave_rows", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -37,7 +37,8 @@ class PlanInfo(ctypes.Structure):
                 ("waves_per_item", ctypes.c_int32), ("items", ctypes.c_int32),
                 ("active_pairs", ctypes.c_int64), ("active_flops", ctypes.c_double),
                 ("io_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
-                ("bound_mode", ctypes.c_int32), ("split_frames", ctypes.c_int32)]
+                ("bound_mode", ctypes.c_int32), ("split_frames", ctypes.c_int32),
+                ("wave_rows", ctypes.c_int32)]
 
 
 class GenericInfo(ctypes.Structure):

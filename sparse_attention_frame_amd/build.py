@@ -6,22 +6,26 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsfa.so")
+OBJ_DIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wno-unused-function",
     # keep the compiler away from packed-fp32 VALU forms
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+
+# Per-source additions to HIPCC_FLAGS (none at present).
+EXTRA_FLAGS: dict = {}
 
 
 def hipcc() -> str:
@@ -35,21 +39,38 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into sparse_attention_frame_amd/libsfa.so (always rebuilds)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           "-I", os.path.join(PKG, "csrc"), *sources(), "-o", tmp]
+# the host pass warns that it does not know the packed-fp32 feature: harmless
+_NOISE = "is not a recognized feature for this target"
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    # the host pass warns that it does not know the packed-fp32 feature: harmless
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(ln for ln in res.stderr.splitlines() if noise not in ln)
+    err = "\n".join(ln for ln in res.stderr.splitlines() if _NOISE not in ln)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into sparse_attention_frame_amd/libsfa.so (always rebuilds)."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+    jobs = []
+    for src in sources():
+        name = os.path.basename(src)
+        obj = os.path.join(OBJ_DIR, name + ".o")
+        jobs.append((obj, [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(name, []), *inc, "-c", src,
+                           "-o", obj]))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(workers) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for _, cmd in jobs]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp],
+         verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -48,13 +48,21 @@ int validate_geometry(const sfa_geometry* g) {
   return SFA_OK;
 }
 
-// Query granules per work item: as many as one workgroup holds (8 query tiles of
-// 32 rows), or the whole frame when it is shorter. The last block of a frame takes
+// Compute units the default block size aims to keep busy (MI355X: 256).
+constexpr int kTargetItems = 256;
+
+// Query granules per work item: as many as one workgroup holds (waves x query tiles
+// of 32 rows), or the whole frame when it is shorter. The last block of a frame takes
 // the remaining rows, so a frame costs ceil(T / 32) wave tiles, the fewest possible
 // (a block size that divides T, such as 240 rows for T = 3600, leaves 16 repeated
-// rows in the last wave tile of every block).
-int auto_block_granules(int t_granules) {
-  return t_granules < kMaxBlockGranules ? t_granules : kMaxBlockGranules;
+// rows in the last wave tile of every block). When that gives fewer work items than
+// compute units (small layers), the block is the largest one that gives every compute
+// unit an item, but not less than one wave's rows.
+int auto_block_granules(int t_granules, int max_granules, int min_granules, int64_t groups) {
+  const int top = t_granules < max_granules ? t_granules : max_granules;
+  for (int gq = top; gq >= min_granules; --gq)
+    if (groups * ((t_granules + gq - 1) / gq) >= kTargetItems) return gq;
+  return top < min_granules ? top : min_granules;
 }
 
 int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out) {
@@ -66,18 +74,25 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   const int tg = T / kGranule;
   const int block_q = opt ? opt->block_q : 0;
   const int waves = (opt && opt->waves_per_item) ? opt->waves_per_item : 8;
-  if (waves != 4 && waves != 8) return SFA_ERR_UNSUPPORTED;
+  if (waves != 4 && waves != 8 && waves != 12) return SFA_ERR_UNSUPPORTED;
+  const int wave_rows = (opt && opt->wave_rows) ? opt->wave_rows : (waves == 4 ? 64 : 32);
+  if (wave_rows != 32 && wave_rows != 64) return SFA_ERR_UNSUPPORTED;
+  if (waves == 4 && wave_rows != 64) return SFA_ERR_UNSUPPORTED;
+  if (waves == 12 && wave_rows != 32) return SFA_ERR_UNSUPPORTED;
+  const int qt = wave_rows / 32;
+  const int max_granules = waves * wave_rows / kGranule;
   const int stages = (opt && opt->lds_stages) ? opt->lds_stages : 3;
-  if (stages < 2 || stages > 4) return SFA_ERR_UNSUPPORTED;
+  if (stages < 2 || stages > (waves == 12 ? 3 : 4)) return SFA_ERR_UNSUPPORTED;
   const int bound_mode = opt ? opt->bound_mode : 0;
   if (bound_mode != 0 && bound_mode != 1) return SFA_ERR_UNSUPPORTED;
   const int key_split = opt ? opt->key_split : 0;
   if (key_split != 0 && key_split != -1) return SFA_ERR_UNSUPPORTED;
   int gq;
   if (block_q == 0) {
-    gq = auto_block_granules(tg);
+    gq = auto_block_granules(tg, max_granules, wave_rows / kGranule,
+                             int64_t(geom->batch) * geom->heads * (geom->frames + 1));
   } else {
-    if (block_q < 0 || block_q % kGranule != 0 || block_q / kGranule > kMaxBlockGranules)
+    if (block_q < 0 || block_q % kGranule != 0 || block_q / kGranule > max_granules)
       return SFA_ERR_UNSUPPORTED;
     gq = block_q / kGranule;
     if (gq > tg) gq = tg;  // one block holds the whole frame
@@ -92,6 +107,7 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   p->S = (F + 1) * T;
   p->gq = gq;
   p->waves = waves;
+  p->qt = qt;
   p->stages = stages;
   p->bound_mode = bound_mode;
   p->nqb = (tg + gq - 1) / gq;  // the last block of a frame may be shorter
@@ -101,9 +117,9 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   // one frame are the last multi-frame items the largest-first order starts, and the
   // longest of the short items that end the launch; each is split into two key halves
   // (frames ordered reference first), so the tail is made of items half as long. Only
-  // the 8-wave kernel (one 32-row query tile per wave) merges halves.
+  // the kernels of 8 or 12 waves merge halves.
   int vmin = 0;
-  if (key_split == 0 && waves == 8)
+  if (key_split == 0 && waves >= 8)
     for (int f = 1; f <= F; ++f) {
       const int v = visible_frames(f, F, w);
       if (v >= 2 && (vmin == 0 || v < vmin)) vmin = v;
@@ -164,11 +180,12 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   const size_t ngran = size_t(p->S) / kGranule;
   p->ws.pkmax = take(ngran * bh * 4);          // [b][h][granule], squared norms
   p->ws.pqmax = take(ngran * bh * 4);
-  p->ws.vt = take(bh * size_t(D) * size_t(p->S) * 2);  // bf16 V^T [b][h][d][S]
+  p->ws.kst = take(bh * size_t(D) * size_t(p->S) * 2);  // bf16 K and V, staged layouts
+  p->ws.vst = take(bh * size_t(D) * size_t(p->S) * 2);
   p->ws.queue = take(kQueueWords * 4);
   const size_t nsplit_items = size_t(nsplit) * bh * p->nqb;
   p->ws.part = take(nsplit_items * 2 * part_floats(D) * 4);
-  p->ws.split_cnt = take(nsplit_items * 4);
+  p->ws.split_cnt = take(nsplit_items * kSplitPasses * 4);
   p->ws.total = off;
   *out = p;
   return SFA_OK;
@@ -208,7 +225,8 @@ NormParams norm_params(const sfa_plan* p, const sfa_tensor& q, const sfa_tensor&
   n.qsb = q.stride_b; n.qss = q.stride_s; n.qsh = q.stride_h;
   n.ksb = k.stride_b; n.kss = k.stride_s; n.ksh = k.stride_h;
   n.vsb = v.stride_b; n.vss = v.stride_s; n.vsh = v.stride_h;
-  n.vt = reinterpret_cast<uint16_t*>(base + p->ws.vt);
+  n.kst = reinterpret_cast<uint16_t*>(base + p->ws.kst);
+  n.vst = reinterpret_cast<uint16_t*>(base + p->ws.vst);
   n.mu = reinterpret_cast<float*>(base + p->ws.mu);
   n.kmax = reinterpret_cast<float*>(base + p->ws.kmax);
   n.qmax = reinterpret_cast<float*>(base + p->ws.qmax);
@@ -224,7 +242,7 @@ NormParams norm_params(const sfa_plan* p, const sfa_tensor& q, const sfa_tensor&
   n.pqmax = reinterpret_cast<float*>(base + p->ws.pqmax);
   n.queue = reinterpret_cast<int32_t*>(base + p->ws.queue);
   n.split_cnt = reinterpret_cast<int32_t*>(base + p->ws.split_cnt);
-  n.nsplit_cnt = p->nsplit * p->g.batch * p->g.heads * p->nqb;
+  n.nsplit_cnt = p->nsplit * p->g.batch * p->g.heads * p->nqb * kSplitPasses;
   n.B = p->g.batch; n.H = p->g.heads; n.S = p->S; n.D = p->g.head_dim;
   n.nchunk = p->nchunk;
   n.T = p->g.tokens_per_frame; n.F = p->g.frames; n.w = p->g.window;
@@ -380,7 +398,8 @@ int sfa_generic_create(const sfa_geometry* geom, sfa_generic** out) {
     off = align256(off + bytes);
     return at;
   };
-  g->ws_vt = take(size_t(bh) * D * size_t(g->S) * 2);
+  g->ws_kst = take(size_t(bh) * D * size_t(g->S) * 2);
+  g->ws_vst = take(size_t(bh) * D * size_t(g->S) * 2);
   g->ws_lists = take(size_t(n ? n : 1) * 4);
   g->ws_offs = take(size_t(2) * (g->nqb + 1) * 4);
   g->ws_part = take(size_t(2) * bh * size_t(g->S) * D * 4);
@@ -447,18 +466,22 @@ int sfa_generic_attention(const sfa_generic* g, sfa_tensor q, sfa_tensor k, sfa_
   if (e != hipSuccess) return hip_status(e);
   NormParams n;
   memset(&n, 0, sizeof(n));
+  n.k = static_cast<const uint16_t*>(k.data);
+  n.ksb = k.stride_b; n.kss = k.stride_s; n.ksh = k.stride_h;
   n.v = static_cast<const uint16_t*>(v.data);
   n.vsb = v.stride_b; n.vss = v.stride_s; n.vsh = v.stride_h;
-  n.vt = reinterpret_cast<uint16_t*>(base + g->ws_vt);
+  n.kst = reinterpret_cast<uint16_t*>(base + g->ws_kst);
+  n.vst = reinterpret_cast<uint16_t*>(base + g->ws_vst);
   n.B = g->g.batch; n.H = g->g.heads; n.S = g->S; n.D = g->g.head_dim;
-  e = sfa_launch_vt(n, s);
+  e = sfa_launch_stage(n, s);
   if (e != hipSuccess) return hip_status(e);
   GenericParams gp;
   gp.q = static_cast<const uint16_t*>(q.data);
   gp.k = static_cast<const uint16_t*>(k.data);
   gp.qsb = q.stride_b; gp.qss = q.stride_s; gp.qsh = q.stride_h;
   gp.ksb = k.stride_b; gp.kss = k.stride_s; gp.ksh = k.stride_h;
-  gp.vt = reinterpret_cast<const uint16_t*>(base + g->ws_vt);
+  gp.kst = reinterpret_cast<const uint16_t*>(base + g->ws_kst);
+  gp.vst = reinterpret_cast<const uint16_t*>(base + g->ws_vst);
   gp.lists = reinterpret_cast<const int32_t*>(base + g->ws_lists);
   gp.offs = reinterpret_cast<const int32_t*>(base + g->ws_offs);
   gp.part = reinterpret_cast<float*>(base + g->ws_part);
@@ -499,6 +522,7 @@ int sfa_plan_get_info(const sfa_plan* p, sfa_plan_info* out) {
   out->workspace_bytes = p->ws.total;
   out->bound_mode = p->bound_mode;
   out->split_frames = p->nsplit;
+  out->wave_rows = 32 * p->qt;
   return SFA_OK;
 }
 
@@ -591,7 +615,8 @@ int sfa_fwd(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_ten
   f.qmu = reinterpret_cast<const float*>(base + p->ws.qmu);
   f.kvis = reinterpret_cast<const float*>(base + p->ws.kvis);
   f.felig = reinterpret_cast<const uint8_t*>(base + p->ws.felig);
-  f.vt = reinterpret_cast<const uint16_t*>(base + p->ws.vt);
+  f.kst = reinterpret_cast<const uint16_t*>(base + p->ws.kst);
+  f.vst = reinterpret_cast<const uint16_t*>(base + p->ws.vst);
   f.B = p->g.batch; f.H = p->g.heads; f.S = p->S; f.T = p->g.tokens_per_frame;
   f.F = p->g.frames; f.w = p->g.window;
   f.gq = p->gq; f.nqb = p->nqb; f.items = p->items;
@@ -601,7 +626,8 @@ int sfa_fwd(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_ten
   f.split_cnt = reinterpret_cast<int32_t*>(base + p->ws.split_cnt);
   memcpy(f.frame_order, p->frame_order, sizeof(f.frame_order));
   return hip_status(
-      sfa_launch_fwd(f, p->g.head_dim, p->waves, p->stages, static_cast<hipStream_t>(stream)));
+      sfa_launch_fwd(f, p->g.head_dim, p->waves, p->qt, p->stages,
+                     static_cast<hipStream_t>(stream)));
 }
 
 int sfa_attention(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_tensor o,

@@ -69,7 +69,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // (1.0, 1.0) in bf16: dot2 with it adds the two halves of a packed pair
 constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
-constexpr int kStageKeys = 64;  // keys per LDS stage (4 granules, 2 tiles of 32)
 
 // Online softmax keeps a stale running maximum until a tile's maximum exceeds it by
 // more than kLazy (log2 units). P then stays below 2^kLazy, which bf16 and the fp32
@@ -95,27 +94,37 @@ __device__ inline void wait_vm() {
 template <int D, int WAVES, int QT, int NBUF>
 struct Attn {
   static constexpr int kThreads = WAVES * 64;
+  // The fixed-maximum path with two query tiles per wave runs every stage, the partial
+  // last one included, through one code shape (masked tail): with 64 query rows a wave's
+  // accumulators, Q and scores fill its 256 registers, and a separate tail would make
+  // the compiler spill them.
+  static constexpr bool kMaskTail = QT == 2;
   static constexpr int KS = D / 16;             // 16-dim k-steps of QK^T
   static constexpr int DT = D / 32;             // 32-dim tiles of O^T
-  static constexpr int CH = D / 8;              // 16-byte chunks per key row
-  static constexpr int ROWB = 2 * D;            // bytes per key row
-  static constexpr int KPR = 256 / ROWB;        // key rows per 256-byte bank sweep
-  static constexpr int STAGE_B = kStageKeys * ROWB;          // bytes per tensor per stage
-  static constexpr int DMA_KEYS = 1024 / ROWB;               // K keys per DMA instruction
-  static constexpr int DMA_N = 2 * STAGE_B / 1024;           // K + V instructions per stage
-  static constexpr int VG_B = D * 32;                        // bytes of one V^T granule
-  static constexpr int DMA_VG = VG_B / 1024;                 // DMA instructions per V^T granule
+  // LDS stages copy the staged HBM layouts (sfa_internal.h) granule by granule:
+  //   K   [granule][16-byte chunk c][16 keys]: the operand of k-step ks for a lane is its
+  //        key's row, chunk 2ks + g, at a fixed lane offset + 512 * ks;
+  //   V^T [granule][d][16 keys], 16-byte halves swizzled by (d / 8) % 2.
+  // 16 lanes reading one chunk of 16 keys, or one half of 16 V^T rows, hit 16 distinct
+  // 16-byte bank groups.
+  static constexpr int GB = sfa::staged_granule_bytes(D);   // bytes of one staged granule
+  // keys per LDS stage: 64 (4 granules, 2 tiles of 32); 96 with 12 waves, so that a
+  // stage's DMA requests split evenly over the waves
+  static constexpr int SK = WAVES == 12 ? 96 : 64;
+  static constexpr int GPS = SK / 16;                        // granules per stage
+  static constexpr int TPS = SK / 32;                        // 32-key tiles per stage
+  static constexpr int STAGE_B = GPS * GB;                   // bytes per tensor per stage
+  static constexpr int DMA_G = GB / 1024;                    // DMA requests per granule
+  static constexpr int DMA_N = 2 * GPS * DMA_G;              // K + V requests per stage
   static constexpr int LDS_BYTES = NBUF * 2 * STAGE_B;       // NBUF stages of K and V
   // LDS layout: K stage buffers [0, NBUF*STAGE_B), V^T stage buffers after them.
   // Lane offsets of V^T reads include VBASE so every operand read is a base
   // register plus an immediate below 64 KB.
   static constexpr int VBASE = NBUF * STAGE_B;
-  static_assert(DMA_N % WAVES == 0, "DMA instructions split evenly over waves");
+  static_assert(DMA_N % WAVES == 0, "DMA requests split evenly over waves");
 
-  static constexpr int DMA_W = DMA_N / WAVES;                // DMA instructions per wave
-  static constexpr int LPR = 64 / DMA_KEYS;                  // lanes per key row
+  static constexpr int DMA_W = DMA_N / WAVES;                // DMA requests per wave
 
-  __device__ static inline int k_phys(int key, int c) { return c ^ ((key / KPR) % CH); }
   __device__ static inline int vt_half(int d, int half) { return half ^ ((d >> 3) & 1); }
   // key fed to S^T MFMA row rho (see the header)
   __device__ static inline int key_of_row(int rho) {
@@ -123,76 +132,52 @@ struct Attn {
     return 16 * (m >> 1) + 8 * gg + 4 * (m & 1) + i;
   }
 
-  __device__ static inline int granule_key(const KeyRanges& r, int gi) {
-    const int t = gi * 16;
-    return t < r.r0_end ? t : r.r1_begin + (t - r.r0_end);
-  }
-
-  // Per-lane constants of the hot loop, computed once per item so that every
-  // LDS read in the loop is base register + immediate and every DMA is a
-  // uniform base + one lane offset.
-  static constexpr int KW = DMA_N / 2 / WAVES;  // K DMA slots per wave per stage
-  static constexpr int VW = DMA_N / 2 / WAVES;  // V^T DMA slots per wave per stage
-  static_assert(KW * WAVES * 2 == DMA_N, "K and V DMA slots split evenly over waves");
-
-  // Per-lane constants of the hot loop, computed once per item so that every
-  // LDS read in the loop is base register + immediate and every DMA is a
-  // uniform (SGPR) base plus one precomputed lane offset.
+  // Per-lane constants of the hot loop: with the staged layouts every LDS read in the
+  // loop is one of these registers plus an immediate, and every DMA request moves
+  // 16 bytes per lane at lane * 16 from a uniform (SGPR) source address.
   struct Lane {
-    uint32_t kofs[KS];       // K operand byte offset inside a stage, per 16-dim k-step
-    uint32_t vofs[DT];       // VBASE + V^T operand offset inside a granule, per 32-dim tile
-    uint32_t kdma[KW];       // K DMA source offset from the stage's first key row
-    uint32_t vdma[VW];       // V^T DMA source offset from the stage's first key column
+    uint32_t kofs;           // K operand byte offset of k-step 0 in a stage's first tile
+    uint32_t vofs;           // VBASE + V^T operand offset inside a granule, 32-dim tile 0
+                             // (tile dt adds dt * 1024, the second 16-key half adds GB)
+    uint32_t dma;            // lane * 16: a lane's bytes in every DMA request
   };
 
-  // Wave-uniform per item: which keys / granules each DMA slot of this wave moves.
+  // Wave-uniform per kernel: the DMA requests of this wave inside a stage. Request
+  // m = wave * DMA_W + i copies 1 KB: tensor m / (DMA_N / 2) (0 K, 1 V), stage granule
+  // (m % (DMA_N / 2)) / DMA_G, kilobyte (m % DMA_G) of that granule.
   struct Slots {
-    int kkey0[KW];           // first stage key of K slot i (DMA_KEYS keys per slot)
-    int vgr[VW];             // stage granule of V^T slot j
-    int kdst[KW];            // LDS byte offset of K slot i inside a stage buffer
-    int vdst[VW];            // LDS byte offset of V^T slot j inside a stage buffer
+    int gi[DMA_W];           // stage granule of request i
+    int src[DMA_W];          // byte offset of request i inside its granule (kilobyte * 1024)
+    int dst[DMA_W];          // LDS byte offset of request i inside a stage buffer
+    bool v[DMA_W];           // request i copies V (else K)
   };
 
-  // Key source of one item: granule gi starts at token 16*gi before the seam
-  // (the end of the first key range) and 16*gi + shift after it.
+  // Key source of one item: granule gi of the item starts at token 16*gi before the
+  // seam (the end of the first key range) and 16*gi + shift after it.
   struct Src {
-    const char* k;           // K row of token 0 of this (b, h)
-    const char* v;           // V^T column of token 0 of this (b, h)
-    int64_t kss2;            // K row stride in bytes
+    const char* k;           // staged K of this (b, h)
+    const char* v;           // staged V of this (b, h)
     int n0;                  // first granule past the seam
-    int shift;               // token shift of granules at or past the seam
+    int gshift;              // granule shift of granules at or past the seam
   };
 
-  __device__ static inline void lane_setup(Lane& L, Slots& W, int64_t kss, int S) {
+  __device__ static inline void lane_setup(Lane& L, Slots& W) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31;
     const int g = lane >> 5;
     const int krow = key_of_row(l32);
+    L.kofs = (krow >> 4) * GB + g * 256 + (krow & 15) * 16;
+    L.vofs = VBASE + l32 * 32 + vt_half(l32, g) * 16;
+    L.dma = lane * 16;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) L.kofs[ks] = krow * ROWB + k_phys(krow, 2 * ks + g) * 16;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 32 * dt + l32;
-      L.vofs[dt] = VBASE + d * 32 + vt_half(d, g) * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < KW; ++i) {  // K rows: lane -> (key, physical chunk)
-      const int key0 = (wave * KW + i) * DMA_KEYS;
-      const int key = key0 + lane / LPR;
-      const int c = k_phys(key, lane % LPR);
-      W.kkey0[i] = key0;
-      W.kdst[i] = key0 * ROWB;
-      L.kdma[i] = uint32_t((key * kss + c * 8) * 2);
-    }
-#pragma unroll
-    for (int j = 0; j < VW; ++j) {  // V^T granule quarter: lane -> (d, physical half)
-      const int m = wave * VW + j;
-      const int gr = m / DMA_VG, qd = m % DMA_VG;
-      const int d = 32 * qd + lane / 2;
-      W.vgr[j] = gr;
-      W.vdst[j] = VBASE + gr * VG_B + qd * 1024;
-      L.vdma[j] = uint32_t((int64_t(d) * S + 16 * gr + 8 * vt_half(d, lane & 1)) * 2);
+    for (int i = 0; i < DMA_W; ++i) {
+      const int m = wave * DMA_W + i;
+      const int r = m % (DMA_N / 2);
+      W.v[i] = m >= DMA_N / 2;
+      W.gi[i] = r / DMA_G;
+      W.src[i] = (r % DMA_G) * 1024;
+      W.dst[i] = (W.v[i] ? VBASE : 0) + W.gi[i] * GB + (r % DMA_G) * 1024;
     }
   }
 
@@ -208,47 +193,32 @@ struct Attn {
   }
 
   // DMA the first `ng` granules of stage s into LDS buffer `buf` (a constant
-  // after unrolling).
+  // after unrolling): every request copies one contiguous kilobyte of a staged granule.
+  // With fill, the stage's other granules receive a copy of its last one (finite
+  // operands for a tile whose second granule is masked).
   __device__ static inline void issue_stage(char* lds, int buf, const Lane& L, const Slots& W,
-                                            const Src& X, int s, int ng) {
-    const int g0 = 4 * s;
-    const char* kst = X.k + int64_t(16 * g0) * X.kss2;
-    const char* vst = X.v + int64_t(16 * g0) * 2;
-    char* lb = lds + buf * STAGE_B;  // + VBASE for V^T (inside vdst)
-    if (g0 >= X.n0 || g0 + ng <= X.n0) {  // one side of the seam: a single base per tensor
-      if (g0 >= X.n0) {
-        kst += int64_t(X.shift) * X.kss2;
-        vst += int64_t(X.shift) * 2;
-      }
+                                            const Src& X, int s, int ng, bool fill = false) {
+    char* lb = lds + buf * STAGE_B;  // + VBASE for V^T (inside dst)
 #pragma unroll
-      for (int i = 0; i < KW; ++i)
-        if (W.kkey0[i] < 16 * ng) dma16(kst, L.kdma[i], lb + W.kdst[i]);
-#pragma unroll
-      for (int j = 0; j < VW; ++j)
-        if (W.vgr[j] < ng) dma16(vst, L.vdma[j], lb + W.vdst[j]);
-    } else {                              // the stage straddles the seam
-#pragma unroll
-      for (int i = 0; i < KW; ++i) {
-        const int gr = W.kkey0[i] / 16;
-        if (gr >= ng) continue;
-        const int sh = g0 + gr >= X.n0 ? X.shift : 0;
-        dma16(kst + int64_t(sh) * X.kss2, L.kdma[i], lb + W.kdst[i]);
-      }
-#pragma unroll
-      for (int j = 0; j < VW; ++j) {
-        if (W.vgr[j] >= ng) continue;
-        const int sh = g0 + W.vgr[j] >= X.n0 ? X.shift : 0;
-        dma16(vst + int64_t(sh) * 2, L.vdma[j], lb + W.vdst[j]);
-      }
+    for (int i = 0; i < DMA_W; ++i) {
+      if (W.gi[i] >= ng && !fill) continue;
+      const int gr = GPS * s + min(W.gi[i], ng - 1);   // granule of the item
+      const int gs = gr >= X.n0 ? gr + X.gshift : gr;  // granule of the (b, h) sequence
+      dma16((W.v[i] ? X.v : X.k) + int64_t(gs) * GB + W.src[i], L.dma, lb + W.dst[i]);
     }
   }
 
-  // One 32-key tile (HALF: only its first 16 keys exist) for all QT query tiles.
-  // kl / vl: LDS byte offsets of the tile's first K and V rows.
+  // One 32-key tile (HALF: only its first 16 keys exist) for the wave's NT query tiles.
+  // kl / vl: LDS byte offsets of the tile's first K and V^T granules.
+  // hi_valid (full tiles only): false when the tile's second granule holds no visible
+  // key (the last stage of an item with an odd granule count, where the DMA has copied a
+  // visible granule in its place so every operand is finite); its 16 weights are then
+  // exp2(-inf) = 0 and add nothing to O or l.
   template <bool HALF, bool ONLINE, int NT>
   __device__ static inline void tile(const char* lds, const Lane& L, int kl, int vl,
                                      const bf16x8 (&qf)[NT][KS], f32x16 (&o)[NT][DT],
-                                     float (&mrow)[NT], float (&lsum)[NT], float cexp) {
+                                     float (&mrow)[NT], float (&lsum)[NT], float cexp,
+                                     bool hi_valid = true) {
     // S^T = K . Q^T
     f32x16 s[NT];
 #pragma unroll
@@ -257,7 +227,7 @@ struct Attn {
       for (int i = 0; i < 16; ++i) s[t][i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + kl + L.kofs[ks]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + kl + L.kofs + 512 * ks);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t][ks], s[t], 0, 0, 0);
@@ -285,10 +255,12 @@ struct Attn {
         }
       }
       const float m = mrow[t];
+      const float mh = hi_valid ? m : __builtin_inff();  // subtrahend of the second granule
 #pragma unroll
       for (int i = 0; i < NV / 2; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t][2 * i], cexp, -m));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t][2 * i + 1], cexp, -m));
+        const float mi = i < 4 ? m : mh;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t][2 * i], cexp, -mi));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t][2 * i + 1], cexp, -mi));
         pk[t][i] = pack_bf16x2(p0, p1);
         // row sum of the bf16 weights that PV uses: p0 + p1 in one dot2
         lsum[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[t][i]),
@@ -300,7 +272,7 @@ struct Attn {
     for (int h = 0; h < (HALF ? 1 : 2); ++h) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + vl + h * VG_B + L.vofs[dt]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + vl + h * GB + dt * 1024 + L.vofs);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const bf16x8 b = __builtin_bit_cast(
@@ -312,12 +284,7 @@ struct Attn {
     }
   }
 
-  // ---- software-pipelined fixed-maximum stage for two query tiles per wave ----
-  // Within a 32-key tile the MFMA work of one query tile overlaps the softmax
-  // VALU work of the other:  QK(q0) | QK(q1) + softmax(q0) + V^T loads |
-  // PV(q0) + softmax(q1) + next K loads | PV(q1). sched_group_barrier pins the
-  // interleave (1 MFMA : 1 LDS read : 6 VALU), which matches 8 MFMAs (256
-  // cycles) with one query tile's softmax (48 VALU).
+  // ---- pieces of the software-pipelined fixed-maximum loop (one query tile per wave) ----
   struct KFrag {
     bf16x8 a[KS];
   };
@@ -327,14 +294,15 @@ struct Attn {
 
   __device__ static inline void load_k(KFrag& f, const char* lds, const Lane& L, int kl) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) f.a[ks] = *reinterpret_cast<const bf16x8*>(lds + kl + L.kofs[ks]);
+    for (int ks = 0; ks < KS; ++ks)
+      f.a[ks] = *reinterpret_cast<const bf16x8*>(lds + kl + L.kofs + 512 * ks);
   }
   __device__ static inline void load_v(VFrag& f, const char* lds, const Lane& L, int vl) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        f.a[h][dt] = *reinterpret_cast<const bf16x8*>(lds + vl + h * VG_B + L.vofs[dt]);
+        f.a[h][dt] = *reinterpret_cast<const bf16x8*>(lds + vl + h * GB + dt * 1024 + L.vofs);
   }
   __device__ static inline f32x16 qk(const KFrag& f, const bf16x8 (&q)[KS]) {
     f32x16 s;
@@ -364,29 +332,6 @@ struct Attn {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[h][dt], b, o[dt], 0, 0, 0);
     }
   }
-  // 8 MFMAs, 8 LDS reads and 48 VALU ops in lock step
-  __device__ static inline void interleave_8() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-    }
-  }
-
-  // One pipelined region: its 16 operand reads first (the other wave of the
-  // SIMD runs its MFMAs meanwhile), then 16 MFMAs with 3 VALU ops behind each
-  // (one 32x32x16 MFMA hides about four plain VALU ops or two exponentials
-  // when two waves share the SIMD).
-  __device__ static inline void interleave_16() {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-    }
-  }
-
   // Region with V^T one region ahead: the 8 K reads of QK(j+1) first, then the 16 MFMAs
   // with 3 VALU ops behind each, and the 8 reads of the next tile's V^T operand placed
   // after the PV MFMAs that consume the same registers.
@@ -398,40 +343,6 @@ struct Attn {
       if (i >= 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read: V^T
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
     }
-  }
-
-  // Both 32-key tiles of one stage (K at kl, V^T at vl), QT == 2, fixed maximum.
-  __device__ static inline void stage2_fixed(const char* lds, const Lane& L, int kl, int vl,
-                                             const bf16x8 (&qf)[2][KS], f32x16 (&o)[2][DT],
-                                             const float (&mrow)[2], float (&lsum)[2],
-                                             float cexp) {
-    KFrag kf;
-    VFrag vf;
-    uint32_t p0[8], p1[8];
-    load_k(kf, lds, L, kl);
-    f32x16 s0 = qk(kf, qf[0]);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      __builtin_amdgcn_sched_barrier(0);
-      // A: QK(q1) + softmax(q0) + V^T loads of this tile
-      f32x16 s1 = qk(kf, qf[1]);
-      softmax_fixed(s0, mrow[0], lsum[0], p0, cexp);
-      load_v(vf, lds, L, vl + tt * 2 * VG_B);
-      interleave_8();
-      __builtin_amdgcn_sched_barrier(0);
-      // B: PV(q0) + softmax(q1) + K loads of the next tile
-      pv(vf, p0, o[0]);
-      softmax_fixed(s1, mrow[1], lsum[1], p1, cexp);
-      if (tt == 0) {
-        load_k(kf, lds, L, kl + 32 * ROWB);
-        interleave_8();
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // C: PV(q1), then QK(q0) of the next tile
-      pv(vf, p1, o[1]);
-      if (tt == 0) s0 = qk(kf, qf[0]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Streams all visible key granules of the item once for NT of the wave's
@@ -447,26 +358,24 @@ struct Attn {
     const KeyRanges r = it.half < 0 ? sfa::key_ranges(it.f, p.F, p.T, p.w)
                                     : sfa::half_key_ranges(it.f, it.half, p.F, p.T, p.w);
     const int ngran = (r.r0_end + (r.r1_end - r.r1_begin)) / 16;
-    const char* kb = reinterpret_cast<const char*>(p.k + it.b * p.ksb + it.h * p.ksh);
-    const char* vtb =
-        reinterpret_cast<const char*>(p.vt + (int64_t(it.b) * p.H + it.h) * D * p.S);
+    const int64_t bh_elems = (int64_t(it.b) * p.H + it.h) * p.S * D;  // staged (b, h) start
 
     const int rows = min(p.gq * 16, p.T - it.qb * p.gq * 16);  // real rows of this item
     const int row0 = it.f * p.T + it.qb * p.gq * 16;
     const int64_t rowstat = (int64_t(it.b) * p.H + it.h) * p.S;
     const float kmax = p.kvis[(int64_t(it.b) * p.H + it.h) * (p.F + 1) + it.f];
-    // a wave whose query tiles hold no real row only helps with the DMA (wave-uniform)
+    // a wave whose query tiles hold no real row only helps with the DMA (wave-uniform);
+    // a second tile without real rows is computed on repeated rows and never stored
     const bool active = __builtin_amdgcn_readfirstlane((wave * QT + t0) * 32) < rows;
 
     Lane L;
     Slots W;
-    lane_setup(L, W, p.kss, p.S);
+    lane_setup(L, W);
     Src X;
-    X.k = kb;
-    X.v = vtb;
-    X.kss2 = p.kss * 2;
+    X.k = reinterpret_cast<const char*>(p.kst + bh_elems);
+    X.v = reinterpret_cast<const char*>(p.vst + bh_elems);
     X.n0 = r.r0_end / 16;
-    X.shift = r.r1_begin - r.r0_end;
+    X.gshift = (r.r1_begin - r.r0_end) / 16;
 
     bf16x8 qf[NT][KS];
     float mrow[NT], lsum[NT];
@@ -488,10 +397,10 @@ struct Attn {
         for (int i = 0; i < 16; ++i) o[t][dt][i] = 0.f;
     }
 
-    const int nfull = ngran / 4;
-    const int rem = ngran - nfull * 4;
+    const int nfull = ngran / GPS;
+    const int rem = ngran - nfull * GPS;
     const int nst = nfull + (rem > 0 ? 1 : 0);
-    if constexpr (!ONLINE && NT == 1 && (NBUF == 3 || NBUF == 4)) {
+    if constexpr (!ONLINE && NT == 1 && TPS == 2 && (NBUF == 3 || NBUF == 4)) {
       // Tile-level software pipeline over the N = 2*nfull full 32-key tiles:
       //   region j:  QK(j+1) + PV(j-1)  (16 MFMAs)  ||  softmax(j)  (48 VALU)
       // Region j reads K(j+1) for its own QK and V^T(j) for the PV of region j+1,
@@ -518,7 +427,7 @@ struct Attn {
         __syncthreads();
 #pragma unroll
         for (int a = 1; a <= AH; ++a)
-          if (a < nst) issue_stage(lds, a, L, W, X, a, a < nfull ? 4 : rem);
+          if (a < nst) issue_stage(lds, a, L, W, X, a, a < nfull ? GPS : rem);
       }
       if (N > 0 && !active) {
         // no real row: the same DMA issues and barriers as the regions below, no compute
@@ -527,7 +436,7 @@ struct Attn {
           wait_stage(sn);
           __syncthreads();
           if (sn + AH < nst)
-            issue_stage(lds, (sn + AH) % NBUF, L, W, X, sn + AH, sn + AH < nfull ? 4 : rem);
+            issue_stage(lds, (sn + AH) % NBUF, L, W, X, sn + AH, sn + AH < nfull ? GPS : rem);
         }
       } else if (N > 0) {
         KFrag kf;
@@ -537,7 +446,7 @@ struct Attn {
         f32x16 scur = qk(kf, qf[0]);
         // region 0: QK(1) + softmax(0)
         __builtin_amdgcn_sched_barrier(0);
-        load_k(kf, lds, L, 32 * ROWB);
+        load_k(kf, lds, L, 2 * GB);
         f32x16 snext = qk(kf, qf[0]);
         load_v(vf, lds, L, 0);  // V^T(0), used by PV(0) in region 1
         softmax_fixed(scur, mrow[0], lsum[0], pprev, p.c);
@@ -554,16 +463,16 @@ struct Attn {
               wait_stage(sn);
               __syncthreads();
               if (sn + AH < nst)
-                issue_stage(lds, (sn + AH) % NBUF, L, W, X, sn + AH, sn + AH < nfull ? 4 : rem);
+                issue_stage(lds, (sn + AH) % NBUF, L, W, X, sn + AH, sn + AH < nfull ? GPS : rem);
             }
             // tile j+1 = 1 + u + 1 and tile j = 1 + u (mod 2*NBUF)
             const int bn = ((u + 2) / 2) % NBUF, tn = (u + 2) & 1;
             const int bc = ((u + 1) / 2) % NBUF, tc = (u + 1) & 1;
             __builtin_amdgcn_sched_barrier(0);
-            load_k(kf, lds, L, bn * STAGE_B + tn * 32 * ROWB);
+            load_k(kf, lds, L, bn * STAGE_B + tn * 2 * GB);
             snext = qk(kf, qf[0]);
             pv(vf, pprev, oo);                                 // V^T(j-1), read last region
-            load_v(vf, lds, L, bc * STAGE_B + tc * 2 * VG_B);  // V^T(j) for the next region
+            load_v(vf, lds, L, bc * STAGE_B + tc * 2 * GB);  // V^T(j) for the next region
             softmax_fixed(scur, mrow[0], lsum[0], pcur, p.c);
             interleave_kv();
             __builtin_amdgcn_sched_barrier(0);
@@ -578,7 +487,7 @@ struct Attn {
           const int b = ((jm / 2) % NBUF);
           pv(vf, pprev, oo);     // V^T(N-2), read in region N-2
           softmax_fixed(scur, mrow[0], lsum[0], pcur, p.c);
-          load_v(vf, lds, L, b * STAGE_B + 2 * VG_B);
+          load_v(vf, lds, L, b * STAGE_B + 2 * GB);
           pv(vf, pcur, oo);
         }
       } else if (nst > 0) {
@@ -595,17 +504,54 @@ struct Attn {
           tile<true, ONLINE, NT>(lds, L, kl, kl, qf, o, mrow, lsum, p.c);
         }
         if (active && rem == 3)
-          tile<true, ONLINE, NT>(lds, L, kl + 32 * ROWB, kl + 2 * VG_B, qf, o, mrow, lsum, p.c);
+          tile<true, ONLINE, NT>(lds, L, kl + 2 * GB, kl + 2 * GB, qf, o, mrow, lsum, p.c);
       }
-    } else {
-    // Stages of 64 keys; NBUF of them in flight. Iteration s waits for stage s
-    // (only the DMAs of younger stages may still be outstanding), crosses one
-    // barrier (stage s visible to all waves, stage s-1's buffer free), refills
-    // that buffer with stage s + NBUF - 1 and computes stage s. The 1..3
-    // granule tail stage is computed after the loop.
+    } else if constexpr (kMaskTail && !ONLINE) {
+      static_assert(GPS == 4, "the masked stage loop takes two tiles per stage");
+    // Stages of 64 keys, NBUF - 1 of them in flight, one code shape for every stage: the
+    // last stage of an item whose granule count is not a multiple of 4 is filled with
+    // copies of its last granule and computed as whole tiles, the copies' weights masked
+    // to zero or the tile skipped. Iteration s waits for stage s (the younger stages'
+    // DMAs may stay in flight), crosses one barrier (stage s visible to all waves, the
+    // buffer of stage s - 1 free), refills that buffer with stage s + NBUF - 1 and
+    // computes stage s; unrolled over the NBUF buffers so that every LDS offset is an
+    // immediate.
 #pragma unroll
     for (int j = 0; j < NBUF - 1; ++j)
-      if (j < nst) issue_stage(lds, j, L, W, X, j, j < nfull ? 4 : rem);
+      if (j < nst) issue_stage(lds, j, L, W, X, j, j < nfull ? GPS : rem, true);
+    for (int s0 = 0; s0 < nst; s0 += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        const int s = s0 + u;
+        if (s >= nst) break;
+        if (s + NBUF - 2 < nst)
+          wait_vm<(NBUF - 2) * DMA_W>();
+        else
+          wait_vm<0>();
+        __syncthreads();
+        const int sn = s + NBUF - 1;
+        if (sn < nst)
+          issue_stage(lds, (u + NBUF - 1) % NBUF, L, W, X, sn, sn < nfull ? GPS : rem, true);
+        if (active) {
+          const int kl = u * STAGE_B;          // K and V^T stage offsets
+          const int ng = s < nfull ? GPS : rem;  // visible granules of this stage (GPS == 4)
+          tile<false, false, NT>(lds, L, kl, kl, qf, o, mrow, lsum, p.c, ng >= 2);
+          if (ng >= 3)
+            tile<false, false, NT>(lds, L, kl + 2 * GB, kl + 2 * GB, qf, o, mrow, lsum, p.c,
+                                   ng == 4);
+        }
+      }
+    }
+    } else {
+    // Stages of 64 keys (the last one holds the 1..3 granules left, if any), NBUF - 1 of
+    // them in flight. Iteration s waits for stage s (only the DMAs of younger full
+    // stages may still be outstanding), crosses one barrier (stage s visible to all
+    // waves, the buffer of stage s - 1 free), refills that buffer with stage
+    // s + NBUF - 1 and computes stage s; unrolled over the NBUF buffers so that every
+    // LDS offset is an immediate. The partial last stage is computed after the loop.
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j)
+      if (j < nst) issue_stage(lds, j, L, W, X, j, j < nfull ? GPS : rem);
 
     for (int s0 = 0; s0 < nfull; s0 += NBUF) {
 #pragma unroll
@@ -619,38 +565,41 @@ struct Attn {
         __syncthreads();
         const int sn = s + NBUF - 1;
         if (sn < nst)
-          issue_stage(lds, (u + NBUF - 1) % NBUF, L, W, X, sn, sn < nfull ? 4 : rem);
+          issue_stage(lds, (u + NBUF - 1) % NBUF, L, W, X, sn, sn < nfull ? GPS : rem);
         if (active) {
           const int kl = u * STAGE_B;  // K and V^T stage offsets
-          if constexpr (!ONLINE && NT == 2) {
-            stage2_fixed(lds, L, kl, kl, qf, o, mrow, lsum, p.c);
-          } else {
-            tile<false, ONLINE, NT>(lds, L, kl, kl, qf, o, mrow, lsum, p.c);
-            tile<false, ONLINE, NT>(lds, L, kl + 32 * ROWB, kl + 2 * VG_B, qf, o, mrow, lsum,
-                                    p.c);
-          }
+#pragma unroll
+          for (int tt = 0; tt < TPS; ++tt)
+            tile<false, ONLINE, NT>(lds, L, kl + tt * 2 * GB, kl + tt * 2 * GB, qf, o, mrow,
+                                    lsum, p.c);
         }
       }
     }
-    if (rem > 0) {
+    if (rem > 0) {  // the 1..GPS-1 granules of the last stage, in buffer nfull % NBUF
       wait_vm<0>();
       __syncthreads();
       if (active) {
-        const int kl = (nfull % NBUF) * STAGE_B;
-        const int vl = kl;
-        if (rem >= 2)
-          tile<false, ONLINE, NT>(lds, L, kl, vl, qf, o, mrow, lsum, p.c);
-        else
-          tile<true, ONLINE, NT>(lds, L, kl, vl, qf, o, mrow, lsum, p.c);
-        if (rem == 3)
-          tile<true, ONLINE, NT>(lds, L, kl + 32 * ROWB, vl + 2 * VG_B, qf, o, mrow, lsum, p.c);
+        // one copy per buffer, so that the LDS offsets stay immediates
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u)
+          if (u == nfull % NBUF) {
+            const int kl = u * STAGE_B;
+#pragma unroll
+            for (int tt = 0; tt < TPS; ++tt) {
+              const int tl = kl + tt * 2 * GB;
+              if (2 * tt + 2 <= rem)
+                tile<false, ONLINE, NT>(lds, L, tl, tl, qf, o, mrow, lsum, p.c);
+              else if (2 * tt + 1 == rem)
+                tile<true, ONLINE, NT>(lds, L, tl, tl, qf, o, mrow, lsum, p.c);
+            }
+          }
       }
     }
 
     }
 
-    if (it.half >= 0) {  // a key half (the plan splits 8-wave items only: NT == 1)
-      if constexpr (NT == 1 && QT == 1) merge_halves(p, it, o[0], lsum[0], mrow[0], rows, row0);
+    if (it.half >= 0) {  // a key half (the plan splits the items of 8 or 12 waves only)
+      if constexpr (WAVES >= 8) merge_halves<NT>(p, it, o, lsum, mrow, rows, row0, t0);
       return;
     }
 
@@ -687,11 +636,13 @@ struct Attn {
   // fence would do the same by writing back and invalidating the whole L2 of the XCD,
   // which costs its other workgroups their cached K and V^T. The second half clears the
   // count for the next launch.
-  __device__ static void merge_halves(const FwdParams& p, const Item& it, const f32x16 (&o)[DT],
-                                      float lpart, float m, int rows, int row0) {
+  template <int NT>
+  __device__ static void merge_halves(const FwdParams& p, const Item& it,
+                                      const f32x16 (&o)[NT][DT], const float (&lpart)[NT],
+                                      const float (&m)[NT], int rows, int row0, int t0) {
     constexpr int PF = sfa::part_floats(D);
-    constexpr int WF = DT * 16 * 64;  // floats of one wave's O
-    constexpr int OL = 8 * WF;        // l of 256 rows, then m
+    constexpr int WF = DT * 16 * 64;                   // floats of one 32-row tile's O
+    constexpr int OL = sfa::kPartRows / 32 * WF;       // l of kPartRows rows, then m
     __shared__ int split_seen;
     // thread index re-read here (an empty asm the compiler cannot see through), so that
     // these lane addresses are not hoisted out of the item loop, where they would stay
@@ -699,58 +650,71 @@ struct Attn {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-    const float l = lpart + __shfl_xor(lpart, 32, 64);
     const int slot = ((it.split * p.B + it.b) * p.H + it.h) * p.nqb + it.qb;
+    const int cnt = slot * sfa::kSplitPasses + t0;  // one counter per pass over the keys
     float* mine = p.part + (int64_t(slot) * 2 + it.half) * PF;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int t = 0; t < NT; ++t) {
+      const int tile = wave * QT + t0 + t;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        __hip_atomic_store(&mine[wave * WF + (dt * 16 + i) * 64 + lane], o[dt][i],
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          __hip_atomic_store(&mine[tile * WF + (dt * 16 + i) * 64 + lane], o[t][dt][i],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float l = lpart[t] + __shfl_xor(lpart[t], 32, 64);
+      if (g == 0) {
+        __hip_atomic_store(&mine[OL + tile * 32 + l32], l, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&mine[OL + sfa::kPartRows + tile * 32 + l32], m[t],
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int row = wave * 32 + l32;
-    if (g == 0) {
-      __hip_atomic_store(&mine[OL + row], l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&mine[OL + 256 + row], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     wait_vm<0>();  // every store of this wave acknowledged
     __syncthreads();
-    if (tid == 0) split_seen = atomicAdd(&p.split_cnt[slot], 1);
+    if (tid == 0) split_seen = atomicAdd(&p.split_cnt[cnt], 1);
     __syncthreads();
     const int first = split_seen == 0;
     __syncthreads();
     if (first) return;
-    if (tid == 0) atomicExch(&p.split_cnt[slot], 0);
-    float* other = p.part + (int64_t(slot) * 2 + (1 - it.half)) * PF;
-    const float lo = __hip_atomic_load(&other[OL + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float mo = __hip_atomic_load(&other[OL + 256 + row], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) atomicExch(&p.split_cnt[cnt], 0);
+    const float* other = p.part + (int64_t(slot) * 2 + (1 - it.half)) * PF;
     const bool h0 = it.half == 0;
-    const float m0 = h0 ? m : mo, m1 = h0 ? mo : m;
-    const float l0 = h0 ? l : lo, l1 = h0 ? lo : l;
-    const float mm = fmaxf(m0, m1);
-    const float s0 = __builtin_amdgcn_exp2f(m0 - mm), s1 = __builtin_amdgcn_exp2f(m1 - mm);
-    const float inv = 1.0f / (l0 * s0 + l1 * s1);
-    if (row >= rows) return;
-    uint16_t* op = p.o + it.b * p.osb + int64_t(row0 + row) * p.oss + it.h * p.osh + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int t = 0; t < NT; ++t) {
+      const int tile = wave * QT + t0 + t;
+      const int row = tile * 32 + l32;
+      const float l = lpart[t] + __shfl_xor(lpart[t], 32, 64);
+      const float lo = __hip_atomic_load(&other[OL + row], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      const float mo = __hip_atomic_load(&other[OL + sfa::kPartRows + row], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      const float m0 = h0 ? m[t] : mo, m1 = h0 ? mo : m[t];
+      const float l0 = h0 ? l : lo, l1 = h0 ? lo : l;
+      const float mm = fmaxf(m0, m1);
+      const float s0 = __builtin_amdgcn_exp2f(m0 - mm), s1 = __builtin_amdgcn_exp2f(m1 - mm);
+      const float inv = 1.0f / (l0 * s0 + l1 * s1);
+      if (row >= rows) continue;
+      uint16_t* op = p.o + it.b * p.osb + int64_t(row0 + row) * p.oss + it.h * p.osh + 4 * g;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float y[4];
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 4 * q4 + u;
-          const float a = o[dt][i];
-          const float b = __hip_atomic_load(&other[wave * WF + (dt * 16 + i) * 64 + lane],
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          y[u] = ((h0 ? a : b) * s0 + (h0 ? b : a) * s1) * inv;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float y[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = 4 * q4 + u;
+            const float a = o[t][dt][i];
+            const float b = __hip_atomic_load(&other[tile * WF + (dt * 16 + i) * 64 + lane],
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            y[u] = ((h0 ? a : b) * s0 + (h0 ? b : a) * s1) * inv;
+          }
+          uint2 wv;
+          wv.x = pack_bf16x2(y[0], y[1]);
+          wv.y = pack_bf16x2(y[2], y[3]);
+          *reinterpret_cast<uint2*>(op + 32 * dt + 8 * q4) = wv;
         }
-        uint2 wv;
-        wv.x = pack_bf16x2(y[0], y[1]);
-        wv.y = pack_bf16x2(y[2], y[3]);
-        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * q4) = wv;
-      }
+    }
   }
 
   // Fixed maximum: every query tile of the wave in one pass over the keys.
@@ -758,8 +722,8 @@ struct Attn {
     run<false, QT>(p, it, lds, 0);
   }
 
-  // Online softmax rescales the accumulators with VALU work, so it holds one
-  // query tile at a time (QT passes over the keys).
+  // Online softmax rescales the accumulators with VALU work, so it holds one query
+  // tile at a time in vector registers (QT passes over the keys).
   __device__ static void run_online(const FwdParams& p, const Item& it, char* lds) {
 #pragma unroll
     for (int t0 = 0; t0 < QT; ++t0) {

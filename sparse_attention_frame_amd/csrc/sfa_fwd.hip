@@ -77,14 +77,24 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, int waves, int stages,
+hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, int waves, int qt, int stages,
                           hipStream_t stream) {
   if (p.items <= 0) return hipSuccess;
+  if (waves == 12) {  // 96-key stages: at most three fit in LDS
+    if (head_dim == 128) return stages == 2 ? launch<128, 12, 1, 2>(p, stream)
+                                            : launch<128, 12, 1, 3>(p, stream);
+    return stages == 2 ? launch<64, 12, 1, 2>(p, stream) : launch<64, 12, 1, 3>(p, stream);
+  }
   if (head_dim == 128) {
     if (waves == 4) {
       if (stages == 2) return launch<128, 4, 2, 2>(p, stream);
       if (stages == 3) return launch<128, 4, 2, 3>(p, stream);
       return launch<128, 4, 2, 4>(p, stream);
+    }
+    if (qt == 2) {
+      if (stages == 2) return launch<128, 8, 2, 2>(p, stream);
+      if (stages == 3) return launch<128, 8, 2, 3>(p, stream);
+      return launch<128, 8, 2, 4>(p, stream);
     }
     if (stages == 2) return launch<128, 8, 1, 2>(p, stream);
     if (stages == 3) return launch<128, 8, 1, 3>(p, stream);
@@ -95,8 +105,12 @@ hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, int waves, int 
     if (stages == 3) return launch<64, 4, 2, 3>(p, stream);
     return launch<64, 4, 2, 4>(p, stream);
   }
+  if (qt == 2) {
+    if (stages == 2) return launch<64, 8, 2, 2>(p, stream);
+    if (stages == 3) return launch<64, 8, 2, 3>(p, stream);
+    return launch<64, 8, 2, 4>(p, stream);
+  }
   if (stages == 2) return launch<64, 8, 1, 2>(p, stream);
   if (stages == 3) return launch<64, 8, 1, 3>(p, stream);
   return launch<64, 8, 1, 4>(p, stream);
 }
-

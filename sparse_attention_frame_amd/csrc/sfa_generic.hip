@@ -20,33 +20,25 @@ struct Generic : Attn<D, 8, 1, 2> {
   using typename A::Slots;
   using A::KS;
   using A::DT;
-  using A::KW;
-  using A::VW;
+  using A::DMA_W;
   using A::STAGE_B;
-  using A::ROWB;
-  using A::VG_B;
+  using A::GB;
   using A::dma16;
   using A::lane_setup;
 
-  // DMA of the 64-key stage starting at key0 of one (b, h); granules past the
-  // end of the sequence are loaded from the last valid granule instead (finite
-  // values; those keys are masked).
+  // DMA of the 64-key stage starting at key0 of one (b, h) from the staged K and V;
+  // granules past the end of the sequence are loaded from the last valid granule
+  // instead (finite values; those keys are masked).
   __device__ static inline void issue_generic(char* lds, int buf, const Lane& L, const Slots& W,
-                                              const char* kbase, int64_t kss2, const char* vbase,
-                                              int key0, int S) {
+                                              const char* kbase, const char* vbase, int key0,
+                                              int S) {
     const int ng = S >> 4;
     char* lb = lds + buf * STAGE_B;
 #pragma unroll
-    for (int i = 0; i < KW; ++i) {
-      const int gk = (key0 + W.kkey0[i]) >> 4;
-      const int sh = gk < ng ? 0 : (ng - 1 - gk) * 16;
-      dma16(kbase + int64_t(key0 + sh) * kss2, L.kdma[i], lb + W.kdst[i]);
-    }
-#pragma unroll
-    for (int j = 0; j < VW; ++j) {
-      const int gv = (key0 >> 4) + W.vgr[j];
-      const int sh = gv < ng ? 0 : (ng - 1 - gv) * 16;
-      dma16(vbase + int64_t(key0 + sh) * 2, L.vdma[j], lb + W.vdst[j]);
+    for (int i = 0; i < DMA_W; ++i) {
+      const int gr = (key0 >> 4) + W.gi[i];
+      const int gs = gr < ng ? gr : ng - 1;
+      dma16((W.v[i] ? vbase : kbase) + int64_t(gs) * GB + W.src[i], L.dma, lb + W.dst[i]);
     }
   }
 
@@ -62,7 +54,7 @@ struct Generic : Attn<D, 8, 1, 2> {
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + kl + L.kofs[ks]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + kl + L.kofs + 512 * ks);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
     }
     if (MASKED) {
@@ -110,7 +102,7 @@ struct Generic : Attn<D, 8, 1, 2> {
           bf16x8, make_uint4(pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + vl + h * VG_B + L.vofs[dt]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + vl + h * GB + dt * 1024 + L.vofs);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[dt], 0, 0, 0);
       }
     }
@@ -143,29 +135,28 @@ struct Generic : Attn<D, 8, 1, 2> {
       for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
     Lane L;
     Slots W;
-    lane_setup(L, W, p.kss, p.S);
-    const char* kbase = reinterpret_cast<const char*>(p.k + b * p.ksb + h * p.ksh);
-    const char* vbase = reinterpret_cast<const char*>(p.vt + int64_t(bh) * D * p.S);
-    const int64_t kss2 = p.kss * 2;
+    lane_setup(L, W);
+    const char* kbase = reinterpret_cast<const char*>(p.kst + int64_t(bh) * D * p.S);
+    const char* vbase = reinterpret_cast<const char*>(p.vst + int64_t(bh) * D * p.S);
     const int32_t* lst = p.lists + p.offs[pass * (p.nqb + 1) + qb];
     const int nst = 2 * (p.offs[pass * (p.nqb + 1) + qb + 1] - p.offs[pass * (p.nqb + 1) + qb]);
-    if (nst > 0) issue_generic(lds, 0, L, W, kbase, kss2, vbase, (lst[0] & 0x3fffffff) * 128, p.S);
+    if (nst > 0) issue_generic(lds, 0, L, W, kbase, vbase, (lst[0] & 0x3fffffff) * 128, p.S);
     for (int st = 0; st < nst; ++st) {
       wait_vm<0>();
       __syncthreads();
       if (st + 1 < nst)
-        issue_generic(lds, (st + 1) & 1, L, W, kbase, kss2, vbase,
+        issue_generic(lds, (st + 1) & 1, L, W, kbase, vbase,
                       (lst[(st + 1) >> 1] & 0x3fffffff) * 128 + ((st + 1) & 1) * 64, p.S);
       const int e = lst[st >> 1];
       const int key0 = (e & 0x3fffffff) * 128 + (st & 1) * 64;
       const int kl = (st & 1) * STAGE_B;
       if (e >> 30) {
         tile_generic<false>(lds, L, kl, kl, qf, o, m, l, p.c, key0, fi, pass, p.S, p.T, p.w);
-        tile_generic<false>(lds, L, kl + 32 * ROWB, kl + 2 * VG_B, qf, o, m, l, p.c, key0 + 32, fi,
+        tile_generic<false>(lds, L, kl + 2 * GB, kl + 2 * GB, qf, o, m, l, p.c, key0 + 32, fi,
                             pass, p.S, p.T, p.w);
       } else {
         tile_generic<true>(lds, L, kl, kl, qf, o, m, l, p.c, key0, fi, pass, p.S, p.T, p.w);
-        tile_generic<true>(lds, L, kl + 32 * ROWB, kl + 2 * VG_B, qf, o, m, l, p.c, key0 + 32, fi,
+        tile_generic<true>(lds, L, kl + 2 * GB, kl + 2 * GB, qf, o, m, l, p.c, key0 + 32, fi,
                            pass, p.S, p.T, p.w);
       }
     }

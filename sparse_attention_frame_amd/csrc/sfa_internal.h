@@ -11,7 +11,7 @@ namespace sfa {
 
 constexpr int kGranule = 16;       // token granule: finest bf16 row tiling of the MFMA
 constexpr int kMaxFrameSlots = 1024;  // F + 1 limit (frame order table travels in kernel args)
-constexpr int kMaxBlockGranules = 16;  // <= 256 query rows per item (8 tiles of 32)
+constexpr int kMaxBlockGranules = 32;  // <= 512 query rows per item (16 tiles of 32)
 constexpr int kNormChunk = 64;     // tokens per block in the norm kernels
 
 // Visible key ranges of one query frame: [0, r0_end) and [r1_begin, r1_end)
@@ -133,14 +133,32 @@ __host__ __device__ inline Item decode_item(int idx, const uint16_t* frame_order
 }
 
 struct Workspace {
-  size_t mu, kmax, qmax, bound, elig, kvis, fbound, felig, qn, qmu, psum, pkmax, pqmax, vt,
-      queue, part, split_cnt, total;
+  size_t mu, kmax, qmax, bound, elig, kvis, fbound, felig, qn, qmu, psum, pkmax, pqmax, kst,
+      vst, queue, part, split_cnt, total;
 };
 
+// Staged copies of K and V that the prologue writes for the attention kernel, in the
+// layout its LDS stages use, so that every DMA request copies 1 KB of contiguous bytes
+// and every MFMA operand read is a base register plus an immediate. Per (b, h) the
+// tokens form 16-key granules of 32 * d bytes each:
+//   K: [granule][16-byte chunk c of the d elements][16 keys]: element (key, e) of a
+//      granule at (e / 8) * 128 + (key % 16) * 8 + e % 8;
+//   V: [granule][d][16 keys], the two 16-byte halves of each d-row swapped when
+//      (d / 8) is odd: element (key, e) at e * 16 + (((key / 8) ^ ((e / 8) & 1)) * 8)
+//      + key % 8.
+// Both are bf16, B * H * S * d elements, in (b, h)-major order.
+__host__ __device__ constexpr int staged_granule_bytes(int d) { return 32 * d; }
+
 // Partial result of one key half of a split item, in floats: O (not normalised) as
-// [wave][32-dim tile][register][lane] for 8 waves, then the row sum l and the
-// maximum m the partial is relative to, 256 rows each.
-__host__ __device__ constexpr int part_floats(int d) { return 8 * (d / 32) * 16 * 64 + 2 * 256; }
+// [32-row query tile][32-dim tile][register][lane] for up to kPartRows rows, then the
+// row sum l and the maximum m they are relative to, kPartRows rows each.
+constexpr int kPartRows = 512;
+// Counters per split item: one per pass over the keys (the online path of a kernel with
+// two query tiles per wave makes one pass per tile).
+constexpr int kSplitPasses = 2;
+__host__ __device__ constexpr int part_floats(int d) {
+  return kPartRows / 32 * (d / 32) * 16 * 64 + 2 * kPartRows;
+}
 
 // Work queue of the attention kernel in the workspace: one counter per XCD, a
 // count of workgroups that found no work left, padding to 64 bytes.
@@ -156,7 +174,8 @@ struct FwdParams {
   const float* qmu;
   const float* kvis;     // [b][h][F+1]: key-norm maximum the rows of each query frame use
   const uint8_t* felig;  // [b][h][F+1]: the items of the query frame take the fixed maximum
-  const uint16_t* vt;  // V^T staged by the prologue: [b][h][d][S]
+  const uint16_t* kst;   // K staged by the prologue (granule layout above)
+  const uint16_t* vst;   // V staged by the prologue (granule layout above)
   int32_t B, H, S, T, F, w;
   int32_t gq;     // query granules per item (the last item of a frame: what is left)
   int32_t nqb;    // items per (frame, batch, head): ceil(T / (16 * gq))
@@ -164,7 +183,7 @@ struct FwdParams {
   float c;        // scale * log2(e)
   int32_t* queue; // kQueueWords counters, zero between launches
   float* part;        // [split item][half] partial results (part_floats(d) each)
-  int32_t* split_cnt; // [split item]: halves finished, zero between launches
+  int32_t* split_cnt; // [split item][pass]: halves finished, zero between launches
   uint16_t frame_order[kMaxFrameSlots];
 };
 
@@ -173,7 +192,8 @@ struct NormParams {
   const uint16_t* k;
   const uint16_t* v;
   int64_t qsb, qss, qsh, ksb, kss, ksh, vsb, vss, vsh;
-  uint16_t* vt;   // V^T staging in the workspace: [b][h][d][S]
+  uint16_t* kst;  // K and V staged for the attention kernels (granule layout above)
+  uint16_t* vst;
   float* mu;
   float* kmax;
   float* qmax;
@@ -204,7 +224,8 @@ struct GenericParams {
   const uint16_t* q;
   const uint16_t* k;
   int64_t qsb, qss, qsh, ksb, kss, ksh;
-  const uint16_t* vt;     // [b][h][d][S]
+  const uint16_t* kst;    // K and V staged (granule layout above)
+  const uint16_t* vst;
   const int32_t* lists;   // key blocks: kb | (full << 30), per (pass, query block)
   const int32_t* offs;    // [2][nqb + 1] offsets into lists
   float* part;            // [2][b][h][S][d] per-pass normalised outputs
@@ -251,7 +272,7 @@ struct sfa_generic {
   int32_t* lists;       // host copy, copied into the workspace on every call
   int32_t nlist;
   int32_t* offs;        // [2][nqb + 1]
-  size_t ws_vt, ws_lists, ws_offs, ws_part, ws_lse, ws_total;
+  size_t ws_kst, ws_vst, ws_lists, ws_offs, ws_part, ws_lse, ws_total;
 };
 
 struct sfa_plan {
@@ -260,6 +281,7 @@ struct sfa_plan {
   int32_t S;
   int32_t gq;       // query granules per item (block_q / 16)
   int32_t waves;    // waves per attention workgroup (4 or 8)
+  int32_t qt;       // 32-row query tiles per wave (1 or 2)
   int32_t stages;   // 64-key LDS stages in flight (2..4)
   int32_t nqb;      // ceil(T / block_q)
   int32_t bound_mode;  // 0: per-head key-norm maximum; 1: per visible frame
@@ -274,9 +296,9 @@ struct sfa_plan {
 
 // Launchers (sfa_norms.hip / sfa_fwd.hip); return a hipError_t.
 hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream);
-hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, int waves, int stages,
+hipError_t sfa_launch_fwd(const sfa::FwdParams& p, int head_dim, int waves, int qt, int stages,
                           hipStream_t stream);
-hipError_t sfa_launch_vt(const sfa::NormParams& p, hipStream_t stream);
+hipError_t sfa_launch_stage(const sfa::NormParams& p, hipStream_t stream);
 hipError_t sfa_launch_fold(const uint16_t* w, const uint16_t* gamma, uint16_t* out, int rows,
                            int cols, hipStream_t stream);
 hipError_t sfa_launch_prologue(const sfa::ProParams& p, hipStream_t stream);

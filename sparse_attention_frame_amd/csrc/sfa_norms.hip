@@ -16,8 +16,10 @@
 //               bound = scale * qmax * kmax; per query frame the key-norm
 //               maximum its rows use (the head's, or the largest over the
 //               frames it sees), its bound and its eligibility flag
-//   5. vt     : V^T [b][h][d][S] staged for the attention kernel, whose PV
-//               operands are then single 16-byte LDS reads
+//   5. stage  : K and V copied into the granule layouts the attention kernel's LDS
+//               stages use (sfa_internal.h): each of its DMA requests then copies
+//               1 KB of contiguous bytes, and its QK^T and PV operands are single
+//               16-byte LDS reads at a fixed lane offset plus an immediate
 #include "sfa_internal.h"
 
 namespace {
@@ -250,38 +252,50 @@ __global__ __launch_bounds__(256) void final_kernel(NormParams p) {
   }
 }
 
-// V^T staging: one block per (64-token chunk, b*H + h). Rows of V are read as
-// 16-byte pieces into an LDS tile [token][d] and written out as 16-byte runs
-// of 8 consecutive tokens of one dimension: vt[b][h][d][s].
+// K and V staged for the attention kernel (layouts in sfa_internal.h): one block per
+// 64 tokens of one (b, h). The rows go through LDS so that both the row reads and the
+// staged writes move whole 16-byte pieces of contiguous memory.
 template <int D>
-__global__ __launch_bounds__(256) void vt_kernel(NormParams p) {
+__global__ __launch_bounds__(256) void stage_kernel(NormParams p) {
   constexpr int CHUNK = 64;
-  constexpr int PITCH = D + 8;  // elements; keeps the column reads off one bank
-  __shared__ __attribute__((aligned(16))) uint16_t tile[CHUNK * PITCH];
+  constexpr int PITCH = D + 8;  // elements; a 16-byte column of 16 rows hits 16 bank groups
+  constexpr int CH = D / 8;     // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) uint16_t tk[CHUNK * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t tv[CHUNK * PITCH];
   const int s0 = blockIdx.x * CHUNK;
   const int bh = blockIdx.y;
   const int b = bh / p.H, h = bh - b * p.H;
-  const int n = min(CHUNK, p.S - s0);
-  const uint16_t* src = p.v + b * p.vsb + h * p.vsh;
-  for (int idx = threadIdx.x; idx < CHUNK * (D / 8); idx += 256) {
-    const int tok = idx / (D / 8), c = idx % (D / 8);
-    if (tok < n)
-      *reinterpret_cast<uint4*>(&tile[tok * PITCH + 8 * c]) =
-          *reinterpret_cast<const uint4*>(src + int64_t(s0 + tok) * p.vss + 8 * c);
+  const int n = min(CHUNK, p.S - s0);  // a multiple of 16
+  const uint16_t* ksrc = p.k + b * p.ksb + h * p.ksh;
+  const uint16_t* vsrc = p.v + b * p.vsb + h * p.vsh;
+  for (int idx = threadIdx.x; idx < CHUNK * CH; idx += 256) {
+    const int tok = idx / CH, c = idx % CH;
+    if (tok < n) {
+      *reinterpret_cast<uint4*>(&tk[tok * PITCH + 8 * c]) =
+          *reinterpret_cast<const uint4*>(ksrc + int64_t(s0 + tok) * p.kss + 8 * c);
+      *reinterpret_cast<uint4*>(&tv[tok * PITCH + 8 * c]) =
+          *reinterpret_cast<const uint4*>(vsrc + int64_t(s0 + tok) * p.vss + 8 * c);
+    }
   }
   __syncthreads();
-  uint16_t* dst = p.vt + int64_t(bh) * D * p.S;
-  for (int idx = threadIdx.x; idx < D * (CHUNK / 8); idx += 256) {
-    const int d = idx / (CHUNK / 8), c = idx % (CHUNK / 8);
-    if (8 * c < n) {  // n is a multiple of 16
-      uint32_t w[4];
+  // the chunk's granules are contiguous in both staged tensors
+  const int64_t base = (int64_t(bh) * p.S + s0) * D;  // elements
+  uint4* kd = reinterpret_cast<uint4*>(p.kst + base);
+  uint4* vd = reinterpret_cast<uint4*>(p.vst + base);
+  const int units = n * CH;  // 16-byte pieces of the chunk in each staged tensor
+  for (int u = threadIdx.x; u < units; u += 256) {
+    // K piece u = (granule * CH + c) * 16 + key: row 16 * granule + key, elements 8c..8c+7
+    const int gk = u / (CH * 16), ck = (u / 16) % CH, key = u % 16;
+    kd[u] = *reinterpret_cast<const uint4*>(&tk[(16 * gk + key) * PITCH + 8 * ck]);
+    // V piece u = (granule * D + e) * 2 + physical half: 8 keys of column e
+    const int gv = u / (2 * D), e = (u / 2) % D, hp = u % 2;
+    const int k0 = 16 * gv + 8 * (hp ^ ((e >> 3) & 1));
+    uint32_t w[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = uint32_t(tile[(8 * c + 2 * j) * PITCH + d]) |
-               (uint32_t(tile[(8 * c + 2 * j + 1) * PITCH + d]) << 16);
-      *reinterpret_cast<uint4*>(dst + int64_t(d) * p.S + s0 + 8 * c) =
-          make_uint4(w[0], w[1], w[2], w[3]);
-    }
+    for (int j = 0; j < 4; ++j)
+      w[j] = uint32_t(tv[(k0 + 2 * j) * PITCH + e]) |
+             (uint32_t(tv[(k0 + 2 * j + 1) * PITCH + e]) << 16);
+    vd[u] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -308,14 +322,14 @@ hipError_t sfa_launch_norms(const sfa::NormParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(final_kernel, dim3(p.B * p.H), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return sfa_launch_vt(p, stream);
+  return sfa_launch_stage(p, stream);
 }
 
-hipError_t sfa_launch_vt(const sfa::NormParams& p, hipStream_t stream) {
-  const dim3 vgrid((p.S + 63) / 64, p.B * p.H);
+hipError_t sfa_launch_stage(const sfa::NormParams& p, hipStream_t stream) {
+  const dim3 sgrid((p.S + 63) / 64, p.B * p.H);
   if (p.D == 128)
-    hipLaunchKernelGGL(vt_kernel<128>, vgrid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(stage_kernel<128>, sgrid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL(vt_kernel<64>, vgrid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(stage_kernel<64>, sgrid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -52,12 +52,26 @@ def test_status_strings(L):
     assert b"unknown" in L.sfa_status_str(7)
 
 
-@pytest.mark.parametrize("name,block_q", [("tiny", 48), ("small", 208), ("720p", 256),
+def _auto_block(T, frames, groups, wave_rows=64, waves=8, target=256):
+    """The default block size, restated: the largest multiple of 16 rows up to one
+    workgroup's rows (waves x wave_rows) and the frame that still gives `target` work
+    items, but at least one wave's rows (or the whole frame when it is shorter)."""
+    top = min(T, waves * wave_rows)
+    for bq in range(top, wave_rows - 1, -16):
+        if groups * -(-T // bq) >= target:
+            return bq
+    return min(top, wave_rows)
+
+
+@pytest.mark.parametrize("name,block_q", [("tiny", 32), ("small", 64), ("720p", 256),
                                           ("1080p", 256), ("stress", 256)])
 def test_plan_query_blocks_cover_the_frame(L, name, block_q):
     wl = W.ALL[name]
     p = Plan.for_workload(wl)
     T = wl.tokens_per_frame
+    assert block_q == _auto_block(T, wl.frames, wl.batch * wl.heads * (wl.frames + 1),
+                                  wave_rows=32)
+    assert p.info["wave_rows"] == 32
     nqb = -(-T // block_q)
     assert p.info["block_q"] == block_q and block_q % 16 == 0
     # blocks of block_q rows, the last one ragged: a frame costs ceil(T / 32) wave tiles
@@ -189,7 +203,7 @@ def test_largest_frame_count_is_accepted(L):
 def test_tile_override_errors(L):
     h = ctypes.c_void_p()
     g = _geom()
-    for bq in (8, 24, 272, -16):     # not a multiple of 16, too large, negative
+    for bq in (8, 24, 528, -16):     # not a multiple of 16, too large, negative
         opt = _lib.PlanOptions(bq, 0, 0)
         assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == \
             _lib.SFA_ERR_UNSUPPORTED, bq
@@ -219,13 +233,37 @@ def test_tile_override_errors(L):
         assert L.sfa_plan_get_info(h, ctypes.byref(info)) == 0
         assert info.bound_mode == mode
         L.sfa_plan_destroy(h)
-    for bq, waves in ((16, 0), (48, 4), (0, 8)):
+    # the default block of this 10-group geometry: the frame (48 rows) does not give 256
+    # items, so one wave's rows (32; 64 with 4 waves, cut to the frame)
+    for bq, waves, want in ((16, 0, 16), (48, 4, 48), (0, 8, 32), (0, 4, 48), (0, 12, 32)):
         opt = _lib.PlanOptions(bq, waves, 3)
         assert L.sfa_plan_create_ex(ctypes.byref(g), ctypes.byref(opt), ctypes.byref(h)) == 0
         info = _lib.PlanInfo()
         assert L.sfa_plan_get_info(h, ctypes.byref(info)) == 0
-        assert info.block_q == (bq or 48) and info.waves_per_item == (waves or 8)
+        assert info.block_q == want and info.waves_per_item == (waves or 8)
+        assert info.wave_rows == (64 if waves == 4 else 32)
         L.sfa_plan_destroy(h)
+    # rows per wave: 32 or 64 with 8 waves, only 64 with 4; the block is at most
+    # waves x rows per wave
+    for waves, rows, ok in ((8, 32, True), (8, 64, True), (0, 32, True), (4, 64, True),
+                            (12, 32, True), (4, 32, False), (12, 64, False), (8, 16, False),
+                            (8, 128, False), (0, -32, False)):
+        opt = _lib.PlanOptions(0, waves, 0, 0, 0, rows)
+        # 64 heads x 5 frames: the default block is the largest, one workgroup's rows
+        st = L.sfa_plan_create_ex(ctypes.byref(_geom(heads=64, tokens_per_frame=1024)),
+                                  ctypes.byref(opt), ctypes.byref(h))
+        assert st == (0 if ok else _lib.SFA_ERR_UNSUPPORTED), (waves, rows)
+        if ok:
+            info = _lib.PlanInfo()
+            assert L.sfa_plan_get_info(h, ctypes.byref(info)) == 0
+            assert info.wave_rows == rows and info.block_q == (waves or 8) * rows
+            L.sfa_plan_destroy(h)
+    opt = _lib.PlanOptions(0, 12, 4)                # 96-key stages: at most three fit in LDS
+    assert L.sfa_plan_create_ex(ctypes.byref(_geom()), ctypes.byref(opt), ctypes.byref(h)) == \
+        _lib.SFA_ERR_UNSUPPORTED
+    opt = _lib.PlanOptions(512, 8, 0, 0, 0, 32)     # more rows than 8 waves of 32 hold
+    assert L.sfa_plan_create_ex(ctypes.byref(_geom(tokens_per_frame=1024)), ctypes.byref(opt),
+                                ctypes.byref(h)) == _lib.SFA_ERR_UNSUPPORTED
     assert L.sfa_plan_create_ex(ctypes.byref(g), None, ctypes.byref(h)) == 0
     L.sfa_plan_destroy(h)
     assert L.sfa_plan_create(None, ctypes.byref(h)) == _lib.SFA_ERR_INVALID

@@ -92,14 +92,17 @@ def test_parity_full(sfa, name):
                                atol=1e-3)
 
 
-def sample_rows(wl, n_random=24, seed=0):
+def sample_rows(wl, block_q=512, n_random=24, seed=0):
     T, S = wl.tokens_per_frame, wl.seq
     rows = set()
+    last = (T - 1) // block_q * block_q    # first row of the frame's last (ragged) block
     for f in range(wl.frames + 1):
-        # frame edges, granule and 256-row block edges, the ragged last block of the frame
-        rows.update({f * T, f * T + 15, f * T + 16, f * T + 255, f * T + 256, f * T + T // 2,
-                     f * T + (T - 1) // 256 * 256 - 1, f * T + (T - 1) // 256 * 256,
+        # frame edges, granule, wave-tile and block edges, the ragged last block of the frame
+        rows.update({f * T, f * T + 15, f * T + 16, f * T + 31, f * T + 32, f * T + 63,
+                     f * T + 64, f * T + 255, f * T + 256, f * T + T // 2,
+                     f * T + block_q - 1, f * T + block_q, f * T + last - 1, f * T + last,
                      (f + 1) * T - 17, (f + 1) * T - 16, (f + 1) * T - 1})
+    rows = {r for r in rows if 0 <= r < S}
     g = np.random.default_rng(seed)
     rows.update(int(x) for x in g.integers(0, S, n_random))
     return np.array(sorted(rows))
@@ -117,7 +120,7 @@ def test_parity_sampled_full_size(sfa, name):
     st, _ = check_stats(sfa, plan, ws, q_np, k_np)
     expect_bad = set(wl.boost_heads)
     assert {h for h in range(wl.heads) if not st["eligible"][0, h]} == expect_bad
-    rows = sample_rows(wl)
+    rows = sample_rows(wl, plan.info["block_q"])
     got_all = out[0, torch.from_numpy(rows).cuda()].float().cpu().numpy()   # [R, H, d]
     for h in range(wl.heads):
         ref = oracle.attention_rows(q_np, k_np, v_np, wl.frames, wl.tokens_per_frame, wl.window,
@@ -128,7 +131,7 @@ def test_parity_sampled_full_size(sfa, name):
 
 @pytest.mark.parametrize("limit", [40.0, -1.0])
 def test_parity_sampled_d64_batch2_many_items(sfa, limit):
-    """d = 64, two sequences, 504 work items (more than one per workgroup, so the
+    """d = 64, two sequences, 576 work items (more than one per workgroup, so the
     persistent workgroups' queues, stealing and counter reset run for this head size too),
     both softmax paths; sampled rows of every (batch, head)."""
     F, T, w, H, d, B = 13, 720, 2, 6, 64, 2
@@ -143,11 +146,13 @@ def test_parity_sampled_d64_batch2_many_items(sfa, limit):
     q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
     plan, out, ws = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit)
     # 256-row query blocks: 256, 256 and a ragged 208 per frame
+    assert plan.info["block_q"] == 256
     assert plan.info["items"] == B * H * (F + 1 + plan.info["split_frames"]) * 3
     st, _ = check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
     assert st["eligible"].all() == (limit > 0)
     rows = np.array(sorted({f * T + r for f in range(F + 1)
-                            for r in (0, 255, 256, 511, 512, 687, 688, T - 1)}
+                            for r in (0, 31, 32, 255, 256, 511, 512, 687, 688, 703, 704,
+                                      T - 1)}
                            | set(g.integers(0, S, 16).tolist())))
     got_all = out[:, torch.from_numpy(rows).cuda()].float().cpu().numpy()   # [B, R, H, d]
     for b in range(B):
@@ -397,13 +402,21 @@ OPTION_GEOMS = [(1, 8, 128, 8, 208, 2), (2, 2, 64, 6, 80, 1)]
                                   dict(block_q=48), dict(block_q=48, waves=4),
                                   dict(block_q=112), dict(block_q=112, lds_stages=2),
                                   dict(block_q=48, lds_stages=4),
-                                  dict(key_split=-1)])
+                                  dict(key_split=-1), dict(wave_rows=32),
+                                  dict(wave_rows=32, lds_stages=4),
+                                  dict(wave_rows=32, block_q=112), dict(block_q=176),
+                                  dict(block_q=80, lds_stages=2), dict(wave_rows=64),
+                                  dict(wave_rows=64, block_q=176),
+                                  dict(wave_rows=64, lds_stages=2), dict(waves=12),
+                                  dict(waves=12, lds_stages=2), dict(waves=12, block_q=112),
+                                  dict(waves=12, block_q=80)])
 @pytest.mark.parametrize("limit", [40.0, -1.0])
 def test_plan_options_parity(sfa, geom_, opts, limit):
-    """Every launch configuration sfa_plan_create_ex offers (4 waves of two query tiles, two
-    or four LDS stages, one-granule query blocks, query blocks that do not divide the frame
-    so that its last block is ragged and some waves hold no real row, no key split), both
-    softmax paths, against the oracle."""
+    """Every launch configuration sfa_plan_create_ex offers (8 waves of one or two query
+    tiles, 4 waves of two, two to four LDS stages, one-granule query blocks, query blocks
+    that do not divide the frame so that its last block is ragged and some waves hold no
+    real row or only one real query tile, no key split), both softmax paths, against the
+    oracle."""
     B, H, d, F, T, w = geom_
     say(f"[plan_options] {geom_} {opts} limit={limit}")
     S = (F + 1) * T
@@ -419,6 +432,8 @@ def test_plan_options_parity(sfa, geom_, opts, limit):
         assert plan.info["block_q"] == min(opts["block_q"], T)
     if "waves" in opts:
         assert plan.info["waves_per_item"] == opts["waves"]
+    if "wave_rows" in opts:
+        assert plan.info["wave_rows"] == opts["wave_rows"]
     ref = oracle.attention(q_np, k_np, v_np, F, T, w)
     assert_close(out.float().cpu().numpy(), ref, "options")
     check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
@@ -436,17 +451,20 @@ def _random_cases(n=24, seed=2024):
         H = int(g.integers(1, 4))
         d = int(g.choice([64, 128]))
         B = int(g.integers(1, 3))
-        waves = int(g.choice([0, 4, 8]))
+        waves = int(g.choice([0, 4, 8, 12]))
         stages = int(g.choice([0, 2, 3, 4]))
         limit = float(g.choice([40.0, -1.0, 40.0]))
-        cases.append((F, T, w, H, d, B, waves, stages, limit))
+        rows = 0 if waves == 4 else int(g.choice([0, 32, 64]))
+        if waves == 12:                      # 96-key stages: 32 rows per wave, <= 3 stages
+            rows, stages = 32, min(stages, 3)
+        cases.append((F, T, w, H, d, B, waves, stages, limit, rows))
     return cases
 
 
-@pytest.mark.parametrize("F,T,w,H,d,B,waves,stages,limit", _random_cases())
-def test_random_geometries_and_options(sfa, F, T, w, H, d, B, waves, stages, limit):
+@pytest.mark.parametrize("F,T,w,H,d,B,waves,stages,limit,rows", _random_cases())
+def test_random_geometries_and_options(sfa, F, T, w, H, d, B, waves, stages, limit, rows):
     say(f"[random] F={F} T={T} w={w} H={H} d={d} B={B} waves={waves} stages={stages} "
-        f"limit={limit}")
+        f"limit={limit} wave_rows={rows}")
     S = (F + 1) * T
     g = np.random.default_rng(F * 7919 + T * 31 + w * 7 + H + d + B)
     q_np = g.standard_normal((B, S, H, d)).astype(np.float32)
@@ -456,20 +474,21 @@ def test_random_geometries_and_options(sfa, F, T, w, H, d, B, waves, stages, lim
     q, k, v = to_dev(q_np, k_np, v_np)
     q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
     plan, out, ws = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit, waves=waves,
-                        lds_stages=stages)
+                        lds_stages=stages, wave_rows=rows)
     ref = oracle.attention(q_np, k_np, v_np, F, T, w)
     assert_close(out.float().cpu().numpy(), ref, "random")
     check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
 
 
 @pytest.mark.parametrize("limit", [40.0, -1.0])
-def test_key_split_halves_merge(sfa, limit):
+@pytest.mark.parametrize("rows,waves", [(0, 0), (64, 8), (32, 12)])
+def test_key_split_halves_merge(sfa, limit, rows, waves):
     """The items of the cheapest multi-frame query frames run as two key halves merged by
     whichever finishes second: both paths match the oracle, the merged rows agree with the
     unsplit run to rounding, rows of the other frames are bitwise those of the unsplit run,
     and two runs are bitwise identical whatever the finishing order."""
     F, T, w, H, d, B = 9, 240, 2, 4, 128, 2
-    say(f"[key_split] limit={limit}")
+    say(f"[key_split] limit={limit} wave_rows={rows} waves={waves}")
     S = (F + 1) * T
     g = np.random.default_rng(91)
     q_np = g.standard_normal((B, S, H, d)).astype(np.float32)
@@ -478,11 +497,14 @@ def test_key_split_halves_merge(sfa, limit):
     v_np = g.standard_normal((B, S, H, d)).astype(np.float32)
     q, k, v = to_dev(q_np, k_np, v_np)
     q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
-    plan, a, _ = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit)
+    plan, a, _ = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit, wave_rows=rows,
+                     waves=waves)
     assert plan.info["split_frames"] == 2        # frames 1 and F see 4 frames, the fewest
-    _, b, _ = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit)
+    _, b, _ = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit, wave_rows=rows,
+                  waves=waves)
     assert torch.equal(a, b)
-    _, whole, _ = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit, key_split=-1)
+    _, whole, _ = run(sfa, (B, H, d, F, T, w), q, k, v, bound_limit=limit, key_split=-1,
+                      wave_rows=rows, waves=waves)
     ref = oracle.attention(q_np, k_np, v_np, F, T, w)
     assert_close(a.float().cpu().numpy(), ref, "split")
     assert_close(whole.float().cpu().numpy(), ref, "whole")
