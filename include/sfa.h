@@ -51,8 +51,11 @@ typedef struct sfa_geometry {
   int32_t tokens_per_frame; /* T >= 16, T % 16 == 0 */
   int32_t window;           /* w >= 0 */
   float scale;              /* softmax scale; 0 selects 1/sqrt(d) */
-  float bound_limit;        /* fixed-max eligibility threshold (40 in the workloads);
-                               a negative value makes every head use the online path */
+  float bound_limit;        /* fixed-max eligibility threshold (40 in the workloads), at most
+                               126 / (2 log2 e) = 43.668 (SFA_ERR_UNSUPPORTED above: a fixed
+                               maximum up to 2 * bound_limit above a row's largest logit
+                               must leave its largest weight a normal float); a negative
+                               value makes every head use the online path */
 } sfa_geometry;
 
 /* A bf16 tensor [B, S, H, d] addressed as
@@ -204,32 +207,40 @@ int sfa_attention_groups(const sfa_plan* group_plan, int32_t groups, sfa_tensor 
                          sfa_tensor v, sfa_tensor o, void* workspace, size_t workspace_bytes,
                          void* stream, void* const* group_streams, int32_t nstreams);
 
-/* Copies per-head statistics out of the workspace after sfa_norms (synchronises
- * the stream). Each output pointer is host memory of B*H entries (mu: B*H*d) or
- * NULL to skip it. bound = scale * max_i ||q_i|| * max_j ||k_j - mu|| (per head in
+/* The sfa_read_* calls copy parts of a workspace that sfa_norms has filled to host
+ * memory and synchronise the stream. workspace_bytes is the size of the workspace
+ * (SFA_ERR_INVALID below the plan's workspace_bytes: nothing is copied). */
+
+/* Per-head statistics. Each output pointer is host memory of B*H entries (mu: B*H*d)
+ * or NULL to skip it. bound = scale * max_i ||q_i|| * max_j ||k_j - mu|| (per head in
  * both bound modes); eligible = 1 when every query frame of the head takes the
  * fixed-maximum path. */
-int sfa_read_head_stats(const sfa_plan* plan, const void* workspace, float* mu, float* kmax,
-                        float* qmax, float* bound, uint8_t* eligible, void* stream);
+int sfa_read_head_stats(const sfa_plan* plan, const void* workspace, size_t workspace_bytes,
+                        float* mu, float* kmax, float* qmax, float* bound, uint8_t* eligible,
+                        void* stream);
 
-/* Copies the per-row half of the norm array after sfa_norms (synchronises the
- * stream): qnorm[b][h][s] = ||q_s|| and qmu[b][h][s] = <q_s, mu_bh>, B*H*S floats
- * each, host memory, either may be NULL. The attention kernel derives the fixed
- * row maximum from them as M = scale * (qmu + qnorm * kvis[b][h][frame(s)]). */
-int sfa_read_row_norms(const sfa_plan* plan, const void* workspace, float* qnorm, float* qmu,
-                       void* stream);
+/* The per-row half of the norm array: qnorm[b][h][s] = ||q_s|| and
+ * qmu[b][h][s] = <q_s, mu_bh>, B*H*S floats each, host memory, either may be NULL. The
+ * attention kernel derives the fixed row maximum from them as
+ * M = scale * (qmu + qnorm * kvis[b][h][frame(s)]). */
+int sfa_read_row_norms(const sfa_plan* plan, const void* workspace, size_t workspace_bytes,
+                       float* qnorm, float* qmu, void* stream);
 
-/* Copies the per-(b, h, query frame) half of the norm array after sfa_norms
- * (synchronises the stream); each output is host memory of B*H*(F+1) entries,
- * index [b][h][g], or NULL to skip it:
+/* The per-(b, h, query frame) half of the norm array; each output is host memory of
+ * B*H*(F+1) entries, index [b][h][g], or NULL to skip it:
  *   kvis[g]     key-norm maximum the rows of query frame g use: bound_mode 0 the
  *               head's max_j ||k_j - mu||; bound_mode 1 the maximum over the frames
  *               g sees of max ||k_j - mu|| within the frame;
  *   bound[g]    scale * (max ||q_i|| over the head, mode 0, or over frame g, mode 1) * kvis[g];
  *   eligible[g] bound[g] <= bound_limit (0 for every frame when bound_limit < 0): the
  *               work items of frame g take the fixed-maximum path. */
-int sfa_read_frame_stats(const sfa_plan* plan, const void* workspace, float* kvis, float* bound,
-                         uint8_t* eligible, void* stream);
+int sfa_read_frame_stats(const sfa_plan* plan, const void* workspace, size_t workspace_bytes,
+                         float* kvis, float* bound, uint8_t* eligible, void* stream);
+
+/* The staged copies of k and v the attention kernel reads (layouts at sfa_norms),
+ * B*H*S*d bf16 each, host memory, either may be NULL. */
+int sfa_read_staged(const sfa_plan* plan, const void* workspace, size_t workspace_bytes,
+                    uint16_t* k_staged, uint16_t* v_staged, void* stream);
 
 /* ---- Fused attention prologue (section "Layout as ABI", Fig. 5) ----
  * The chain that produces the attention's inputs -- normalisation, projection,

@@ -15,7 +15,9 @@ What it computes, in float64:
   as -inf logits: the plain definition that the single-pass, no-predicate
   kernel reaches exactly (blocks are either entirely inside the mask or
   entirely skipped, and the reference frame's blocks are ordinary blocks of
-  the same softmax).
+  the same softmax); ``attention_block`` is its unit of work, a block of rows
+  of one (batch, head) inside one query frame, which the full-size tests run
+  over a thread pool.
 * ``head_stats`` -- per (batch, head): the key mean, the largest mean-centred
   key norm, the largest query norm, the Cauchy-Schwarz bound and the
   eligibility flag for the fixed-maximum path.
@@ -40,6 +42,7 @@ frame). No function here is "parity unpinned".
 """
 from .attention import (  # noqa: F401
     attention,
+    attention_block,
     attention_rows,
     frame_row_offsets,
     frame_stats,

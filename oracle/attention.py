@@ -51,6 +51,24 @@ def _default_scale(d: int, scale) -> float:
     return 1.0 / np.sqrt(d) if scale is None or scale == 0 else float(scale)
 
 
+def attention_block(qh, kh, vh, frames: int, tokens_per_frame: int, window: int,
+                    r0: int, r1: int, scale=None):
+    """Rows r0 .. r1-1 of one (batch, head), all inside one query frame: the same
+    definition as ``attention`` (dense logits, the mask as -inf, softmax, times v).
+
+    qh, kh, vh: arrays [S, d] of one (batch, head). Returns float64 [r1 - r0, d].
+    """
+    S, d = kh.shape
+    T = tokens_per_frame
+    f = r0 // T
+    assert (r1 - 1) // T == f, "a block lies inside one query frame"
+    sc = _default_scale(d, scale)
+    visible = np.isin(np.arange(S) // T, key_frames(f, frames, window))
+    s = sc * (np.asarray(qh[r0:r1], dtype=np.float64) @ np.asarray(kh, dtype=np.float64).T)
+    s[:, ~visible] = -np.inf
+    return _softmax_rows(s) @ np.asarray(vh, dtype=np.float64)
+
+
 def attention(q, k, v, frames: int, tokens_per_frame: int, window: int, scale=None):
     """O = softmax(scale * q k^T + mask) v for every (batch, head), float64.
 
@@ -63,17 +81,13 @@ def attention(q, k, v, frames: int, tokens_per_frame: int, window: int, scale=No
     B, S, H, d = q.shape
     T = tokens_per_frame
     assert S == (frames + 1) * T
-    sc = _default_scale(d, scale)
-    frame_of_key = np.arange(S) // T
     out = np.empty((B, S, H, d), dtype=np.float64)
     for f in range(frames + 1):
-        visible = np.isin(frame_of_key, key_frames(f, frames, window))
-        rows = slice(f * T, (f + 1) * T)
         for b in range(B):
             for h in range(H):
-                s = sc * (q[b, rows, h, :] @ k[b, :, h, :].T)  # [T, S]
-                s[:, ~visible] = -np.inf
-                out[b, rows, h, :] = _softmax_rows(s) @ v[b, :, h, :]
+                out[b, f * T:(f + 1) * T, h, :] = attention_block(
+                    q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], frames, T, window,
+                    f * T, (f + 1) * T, scale)
     return out
 
 

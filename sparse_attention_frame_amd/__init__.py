@@ -29,4 +29,6 @@ from .api import (  # noqa: F401
     sfa_read_frame_stats,
     sfa_read_head_stats,
     sfa_read_row_norms,
+    sfa_read_staged,
+    staged,
 )

@@ -59,6 +59,7 @@ EXPORTS = (
     "sfa_plan_create", "sfa_plan_create_ex", "sfa_plan_destroy", "sfa_plan_get_info",
     "sfa_plan_key_ranges", "sfa_plan_item", "sfa_plan_item_keys", "sfa_norms", "sfa_fwd", "sfa_attention",
     "sfa_attention_groups", "sfa_read_head_stats", "sfa_read_row_norms", "sfa_read_frame_stats",
+    "sfa_read_staged",
     "sfa_prologue_fold", "sfa_qkv_prologue",
     "sfa_generic_create", "sfa_generic_destroy", "sfa_generic_get_info", "sfa_generic_block_class",
     "sfa_generic_attention", "sfa_status_str",
@@ -95,9 +96,12 @@ def _declare(lib):
         "sfa_attention_groups": (ctypes.c_int, [P, ctypes.c_int32, Tensor, Tensor, Tensor, Tensor,
                                                 P, ctypes.c_size_t, P, ctypes.POINTER(P),
                                                 ctypes.c_int32]),
-        "sfa_read_head_stats": (ctypes.c_int, [P, P, f32p, f32p, f32p, f32p, u8p, P]),
-        "sfa_read_row_norms": (ctypes.c_int, [P, P, f32p, f32p, P]),
-        "sfa_read_frame_stats": (ctypes.c_int, [P, P, f32p, f32p, u8p, P]),
+        "sfa_read_head_stats": (ctypes.c_int, [P, P, ctypes.c_size_t, f32p, f32p, f32p, f32p,
+                                               u8p, P]),
+        "sfa_read_row_norms": (ctypes.c_int, [P, P, ctypes.c_size_t, f32p, f32p, P]),
+        "sfa_read_frame_stats": (ctypes.c_int, [P, P, ctypes.c_size_t, f32p, f32p, u8p, P]),
+        "sfa_read_staged": (ctypes.c_int, [P, P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint16),
+                                           ctypes.POINTER(ctypes.c_uint16), P]),
         "sfa_prologue_fold": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32, P]),
         "sfa_qkv_prologue": (ctypes.c_int, [ctypes.POINTER(PrologueGeometry), Tensor, P, P, P,
                                             Tensor, Tensor, Tensor, P]),

@@ -197,7 +197,7 @@ def sfa_read_head_stats(plan: Plan, workspace, stream=None):
     bound = np.empty((g.batch, g.heads), np.float32)
     elig = np.empty((g.batch, g.heads), np.uint8)
     f = ctypes.POINTER(ctypes.c_float)
-    check(lib().sfa_read_head_stats(plan.handle, _ws_args(workspace)[0],
+    check(lib().sfa_read_head_stats(plan.handle, *_ws_args(workspace),
                                     mu.ctypes.data_as(f), kmax.ctypes.data_as(f),
                                     qmax.ctypes.data_as(f), bound.ctypes.data_as(f),
                                     elig.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
@@ -211,7 +211,7 @@ def sfa_read_row_norms(plan: Plan, workspace, stream=None):
     qn = np.empty((g.batch, g.heads, plan.seq), np.float32)
     qmu = np.empty((g.batch, g.heads, plan.seq), np.float32)
     f = ctypes.POINTER(ctypes.c_float)
-    check(lib().sfa_read_row_norms(plan.handle, _ws_args(workspace)[0],
+    check(lib().sfa_read_row_norms(plan.handle, *_ws_args(workspace),
                                    qn.ctypes.data_as(f), qmu.ctypes.data_as(f),
                                    _stream_ptr(stream)), "sfa_read_row_norms")
     return qn, qmu
@@ -225,11 +225,25 @@ def sfa_read_frame_stats(plan: Plan, workspace, stream=None):
     bound = np.empty(shape, np.float32)
     elig = np.empty(shape, np.uint8)
     f = ctypes.POINTER(ctypes.c_float)
-    check(lib().sfa_read_frame_stats(plan.handle, _ws_args(workspace)[0],
+    check(lib().sfa_read_frame_stats(plan.handle, *_ws_args(workspace),
                                      kvis.ctypes.data_as(f), bound.ctypes.data_as(f),
                                      elig.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
                                      _stream_ptr(stream)), "sfa_read_frame_stats")
     return {"kvis": kvis, "bound": bound, "eligible": elig.astype(bool)}
+
+
+def sfa_read_staged(plan: Plan, workspace, stream=None):
+    """The staged k and v the attention kernel reads: two uint16 arrays [B, H, S * d] in
+    the granule layouts described at sfa_norms (bf16 bit patterns)."""
+    g = plan.geometry
+    shape = (g.batch, g.heads, plan.seq * g.head_dim)
+    kst = np.empty(shape, np.uint16)
+    vst = np.empty(shape, np.uint16)
+    u16 = ctypes.POINTER(ctypes.c_uint16)
+    check(lib().sfa_read_staged(plan.handle, *_ws_args(workspace), kst.ctypes.data_as(u16),
+                                vst.ctypes.data_as(u16), _stream_ptr(stream)),
+          "sfa_read_staged")
+    return kst, vst
 
 
 def sfa_prologue_fold(w, gamma, stream=None):
@@ -358,6 +372,7 @@ attention_groups = sfa_attention_groups
 head_stats = sfa_read_head_stats
 row_norms = sfa_read_row_norms
 frame_stats = sfa_read_frame_stats
+staged = sfa_read_staged
 generic_attention = sfa_generic_attention
 prologue_fold = sfa_prologue_fold
 qkv_prologue = sfa_qkv_prologue

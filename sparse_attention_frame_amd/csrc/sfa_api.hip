@@ -30,6 +30,9 @@ int hip_status(hipError_t e) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// 126 / (2 * log2(e)): the largest eligibility threshold whose weights stay normal floats
+constexpr float kMaxBoundLimit = 43.668f;
+
 int validate_geometry(const sfa_geometry* g) {
   if (!g) return SFA_ERR_INVALID;
   if (g->batch < 1 || g->heads < 1 || g->frames < 0 || g->window < 0 ||
@@ -37,6 +40,10 @@ int validate_geometry(const sfa_geometry* g) {
     return SFA_ERR_INVALID;
   if (!(g->scale >= 0.0f) || !isfinite(g->scale) || isnan(g->bound_limit))
     return SFA_ERR_INVALID;
+  // a fixed maximum more than 2 * bound_limit above the largest logit would let the
+  // largest weight of a row underflow: exp2(-2 * log2(e) * bound_limit) must stay a
+  // normal float (>= 2^-126)
+  if (g->bound_limit > kMaxBoundLimit) return SFA_ERR_UNSUPPORTED;
   if (g->head_dim != 64 && g->head_dim != 128) return SFA_ERR_UNSUPPORTED;
   if (g->tokens_per_frame % kGranule != 0) return SFA_ERR_UNSUPPORTED;
   if (g->frames + 1 > kMaxFrameSlots) return SFA_ERR_UNSUPPORTED;
@@ -693,9 +700,10 @@ int sfa_attention_groups(const sfa_plan* p, int32_t groups, sfa_tensor q, sfa_te
   return st;
 }
 
-int sfa_read_head_stats(const sfa_plan* p, const void* ws, float* mu, float* kmax, float* qmax,
-                        float* bound, uint8_t* eligible, void* stream) {
-  if (!p || !ws) return SFA_ERR_INVALID;
+int sfa_read_head_stats(const sfa_plan* p, const void* ws, size_t ws_bytes, float* mu,
+                        float* kmax, float* qmax, float* bound, uint8_t* eligible,
+                        void* stream) {
+  if (!p || !ws || ws_bytes < p->ws.total) return SFA_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char* base = static_cast<const char*>(ws);
   const size_t bh = size_t(p->g.batch) * p->g.heads;
@@ -715,9 +723,9 @@ int sfa_read_head_stats(const sfa_plan* p, const void* ws, float* mu, float* kma
   return hip_status(hipStreamSynchronize(s));
 }
 
-int sfa_read_frame_stats(const sfa_plan* p, const void* ws, float* kvis, float* bound,
-                         uint8_t* eligible, void* stream) {
-  if (!p || !ws) return SFA_ERR_INVALID;
+int sfa_read_frame_stats(const sfa_plan* p, const void* ws, size_t ws_bytes, float* kvis,
+                         float* bound, uint8_t* eligible, void* stream) {
+  if (!p || !ws || ws_bytes < p->ws.total) return SFA_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char* base = static_cast<const char*>(ws);
   const size_t n = size_t(p->g.batch) * p->g.heads * size_t(p->g.frames + 1);
@@ -734,9 +742,9 @@ int sfa_read_frame_stats(const sfa_plan* p, const void* ws, float* kvis, float* 
   return hip_status(hipStreamSynchronize(s));
 }
 
-int sfa_read_row_norms(const sfa_plan* p, const void* ws, float* qnorm, float* qmu,
-                       void* stream) {
-  if (!p || !ws) return SFA_ERR_INVALID;
+int sfa_read_row_norms(const sfa_plan* p, const void* ws, size_t ws_bytes, float* qnorm,
+                       float* qmu, void* stream) {
+  if (!p || !ws || ws_bytes < p->ws.total) return SFA_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char* base = static_cast<const char*>(ws);
   const size_t bytes = size_t(p->g.batch) * p->g.heads * size_t(p->S) * 4;
@@ -744,6 +752,20 @@ int sfa_read_row_norms(const sfa_plan* p, const void* ws, float* qnorm, float* q
   if (qnorm) e = hipMemcpyAsync(qnorm, base + p->ws.qn, bytes, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess && qmu)
     e = hipMemcpyAsync(qmu, base + p->ws.qmu, bytes, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return hip_status(e);
+}
+
+int sfa_read_staged(const sfa_plan* p, const void* ws, size_t ws_bytes, uint16_t* k_staged,
+                    uint16_t* v_staged, void* stream) {
+  if (!p || !ws || ws_bytes < p->ws.total) return SFA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* base = static_cast<const char*>(ws);
+  const size_t bytes = size_t(p->g.batch) * p->g.heads * size_t(p->S) * p->g.head_dim * 2;
+  hipError_t e = hipSuccess;
+  if (k_staged) e = hipMemcpyAsync(k_staged, base + p->ws.kst, bytes, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && v_staged)
+    e = hipMemcpyAsync(v_staged, base + p->ws.vst, bytes, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   return hip_status(e);
 }

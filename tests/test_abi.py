@@ -299,6 +299,40 @@ def test_call_validation_happens_before_any_launch(L):
                      need, None) == _lib.SFA_ERR_UNSUPPORTED
 
 
+def test_read_calls_check_the_workspace_size(L):
+    """The sfa_read_* calls refuse a null or too-small workspace before copying anything
+    (the copies would read past the allocation); this runs on CPU."""
+    p = Plan(1, 2, 64, 4, 48, 1)
+    need = p.info["workspace_bytes"]
+    ws = ctypes.c_void_p(1 << 20)
+    f = (ctypes.c_float * 4096)()
+    u8 = (ctypes.c_uint8 * 64)()
+    u16 = (ctypes.c_uint16 * 64)()
+    for size, wsp in ((need - 1, ws), (0, ws), (need, None)):
+        assert L.sfa_read_head_stats(p.handle, wsp, size, f, f, f, f, u8, None) == \
+            _lib.SFA_ERR_INVALID
+        assert L.sfa_read_row_norms(p.handle, wsp, size, f, f, None) == _lib.SFA_ERR_INVALID
+        assert L.sfa_read_frame_stats(p.handle, wsp, size, f, f, u8, None) == \
+            _lib.SFA_ERR_INVALID
+        assert L.sfa_read_staged(p.handle, wsp, size, u16, u16, None) == _lib.SFA_ERR_INVALID
+    assert L.sfa_read_staged(None, ws, need, u16, u16, None) == _lib.SFA_ERR_INVALID
+
+
+def test_bound_limit_cap(L):
+    """bound_limit above 126 / (2 log2 e) would let the largest weight of a row underflow
+    on the fixed-maximum path; the plan refuses it (negative limits force the online
+    path and stay valid)."""
+    cap = 126.0 / (2.0 * np.log2(np.e))
+    h = ctypes.c_void_p()
+    for lim, want in ((40.0, 0), (43.66, 0), (-1.0, 0), (-1e30, 0), (43.68, -2), (100.0, -2),
+                      (float("inf"), -2), (float("nan"), -1)):
+        st = L.sfa_plan_create(ctypes.byref(_geom(bound_limit=lim)), ctypes.byref(h))
+        assert st == want, (lim, st)
+        if st == 0:
+            L.sfa_plan_destroy(h)
+    assert 43.66 < cap < 43.68
+
+
 def test_head_group_call_validation_happens_before_any_launch(L):
     """sfa_attention_groups rejects bad arguments without touching the GPU (this runs on CPU)."""
     p = Plan(1, 2, 64, 4, 48, 1)

@@ -4,6 +4,7 @@ Tolerance for bf16 inputs with fp32 accumulation: max |O_gpu - O_oracle| <= 2e-2
 and ||O_gpu - O_oracle||_2 / ||O_oracle||_2 <= 5e-3; the per-head eligibility
 flag of the fixed-maximum path must match the oracle exactly.
 """
+import os
 import sys
 
 import numpy as np
@@ -108,9 +109,41 @@ def sample_rows(wl, block_q=512, n_random=24, seed=0):
     return np.array(sorted(rows))
 
 
+def oracle_heads(q_np, k_np, v_np, wl, heads, block=1024, workers=None):
+    """Every row of the chosen heads of batch 0 from the oracle, computed as blocks of at
+    most `block` rows inside one query frame (oracle.attention_block) on a thread pool
+    with one BLAS thread per worker. Returns {head: float64 [S, d]}."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    T = wl.tokens_per_frame
+    per_head = {h: tuple(np.ascontiguousarray(x[0, :, h, :], dtype=np.float64)
+                         for x in (q_np, k_np, v_np)) for h in heads}
+    out = {h: np.empty((wl.seq, wl.head_dim)) for h in heads}
+    jobs = [(h, r0, min(r0 + block, (f + 1) * T)) for h in heads
+            for f in range(wl.frames + 1) for r0 in range(f * T, (f + 1) * T, block)]
+
+    def work(job):
+        h, r0, r1 = job
+        qh, kh, vh = per_head[h]
+        out[h][r0:r1] = oracle.attention_block(qh, kh, vh, wl.frames, T, wl.window, r0, r1)
+
+    workers = workers or max(1, min(16, os.cpu_count() or 1))
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+        list(ex.map(work, jobs))
+    return out
+
+
+# whole heads compared at full size: one fixed-maximum head, and on the stress layers one
+# head of the online path too
+FULL_HEADS = {"720p": (0,), "1080p": (0,), "stress": (0, 3), "stress_w13": (0, 3)}
+
+
 @pytest.mark.parametrize("name", ["720p", "1080p", "stress", "stress_w13"])
 def test_parity_sampled_full_size(sfa, name):
-    """Full-size inputs in the benchmark's launch configuration; sampled rows of every head."""
+    """Full-size inputs in the benchmark's launch configuration: every row of whole heads
+    (FULL_HEADS) and sampled rows of every other head."""
     wl = W.ALL[name]
     say(f"[parity_sampled] {name} generating inputs")
     q_np, k_np, v_np = W.make_inputs_np(wl)
@@ -123,10 +156,22 @@ def test_parity_sampled_full_size(sfa, name):
     rows = sample_rows(wl, plan.info["block_q"])
     got_all = out[0, torch.from_numpy(rows).cuda()].float().cpu().numpy()   # [R, H, d]
     for h in range(wl.heads):
+        if h in FULL_HEADS[name]:
+            continue
         ref = oracle.attention_rows(q_np, k_np, v_np, wl.frames, wl.tokens_per_frame, wl.window,
                                     0, h, rows)
         assert_close(got_all[:, h], ref, f"{name} head {h} ({len(rows)} rows)")
     assert torch.isfinite(out.float()).all()
+    say(f"[parity_sampled] {name} oracle on whole heads {FULL_HEADS[name]}")
+    full = oracle_heads(q_np, k_np, v_np, wl, FULL_HEADS[name])
+    got = out[0].float().cpu().numpy()
+    for h, ref in full.items():
+        assert_close(got[:, h], ref, f"{name} head {h} (all {wl.seq} rows)")
+        # and frame by frame, so no frame hides behind the others
+        T = wl.tokens_per_frame
+        for f in range(wl.frames + 1):
+            assert_close(got[f * T:(f + 1) * T, h], ref[f * T:(f + 1) * T],
+                         f"{name} head {h} frame {f}")
 
 
 @pytest.mark.parametrize("limit", [40.0, -1.0])
@@ -264,8 +309,26 @@ def test_zero_query_gives_window_mean(sfa):
         assert_close(got[0, f * T:(f + 1) * T], np.broadcast_to(mean, (T, H, d)), f"frame {f}")
 
 
+def staged_reference(x, d):
+    """The staged layouts of sfa_norms restated on the host from a [B, S, H, d] array
+    (uint16 bf16 bit patterns): K as [granule][8-element chunk][16 keys][8] and V as
+    [granule][d][16 keys] with the 8-key halves of row e swapped when (e / 8) is odd."""
+    B, S, H, _ = x.shape
+    G = S // 16
+    xt = x.transpose(0, 2, 1, 3).reshape(B, H, G, 16, d)          # [b, h, g, key, e]
+    k = xt.reshape(B, H, G, 16, d // 8, 8).transpose(0, 1, 2, 4, 3, 5)
+    v = xt.transpose(0, 1, 2, 4, 3).reshape(B, H, G, d, 2, 8)     # [b, h, g, e, half, 8]
+    swap = ((np.arange(d) >> 3) & 1).astype(bool)
+    v = v.copy()
+    v[:, :, :, swap] = v[:, :, :, swap][:, :, :, :, ::-1]
+    return k.reshape(B, H, S * d), v.reshape(B, H, S * d)
+
+
 def test_double_run_is_bitwise_identical(sfa):
-    """Two runs of one build must agree bit for bit before differences are trusted."""
+    """Two runs of one build must agree bit for bit before differences are trusted: the
+    output and every array the prologue writes for the kernel (head and per-frame stats,
+    row norms, staged K and V), read through the ABI; the staged copies are exactly the
+    inputs in the documented layouts."""
     wl = W.SMALL
     say("[determinism] small")
     q, k, v = to_dev(*W.make_inputs_np(wl))
@@ -277,8 +340,20 @@ def test_double_run_is_bitwise_identical(sfa):
     sa, sb = sfa.head_stats(pa, wa), sfa.head_stats(pa, wb)
     for key in sa:
         np.testing.assert_array_equal(sa[key], sb[key])
+    fa, fb = sfa.frame_stats(pa, wa), sfa.frame_stats(pa, wb)
+    for key in fa:
+        np.testing.assert_array_equal(fa[key], fb[key])
     for x, y in zip(sfa.row_norms(pa, wa), sfa.row_norms(pa, wb)):
         np.testing.assert_array_equal(x, y)
+    ka, va = sfa.staged(pa, wa)
+    kb, vb = sfa.staged(pa, wb)
+    np.testing.assert_array_equal(ka, kb)
+    np.testing.assert_array_equal(va, vb)
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    kr, _ = staged_reference(bits(k), wl.head_dim)
+    _, vr = staged_reference(bits(v), wl.head_dim)
+    np.testing.assert_array_equal(ka, kr)
+    np.testing.assert_array_equal(va, vr)
 
 
 @pytest.mark.parametrize("name", ["small", "720p"])
@@ -349,10 +424,12 @@ def test_error_paths_on_device(sfa):
                                                   ("720p", 3, 3)])
 def test_head_groups_are_bitwise_equal(sfa, name, groups, nstreams):
     """Head groups on their own streams (section "Hiding collectives": heads are
-    independent) give exactly the single-launch result."""
+    independent) match the oracle (every element on the small layer, sampled rows of every
+    head, hence of every group, at 720p) and give exactly the single-launch result."""
     wl = W.ALL[name]
     say(f"[head_groups] {name} groups={groups} streams={nstreams}")
-    q, k, v = to_dev(*W.make_inputs_np(wl))
+    q_np, k_np, v_np = W.make_inputs_np(wl)
+    q, k, v = to_dev(q_np, k_np, v_np)
     _, full, _ = run(sfa, geom(wl), q, k, v)
     gp = sfa.Plan(wl.batch, wl.heads // groups, wl.head_dim, wl.frames, wl.tokens_per_frame,
                   wl.window)
@@ -361,6 +438,17 @@ def test_head_groups_are_bitwise_equal(sfa, name, groups, nstreams):
         out, _ = sfa.attention_groups(gp, groups, q, k, v, streams=streams)
         torch.cuda.synchronize()
         assert torch.equal(out, full), rep
+    if name == "small":
+        ref = oracle.attention(q_np, k_np, v_np, wl.frames, wl.tokens_per_frame, wl.window)
+        assert_close(out.float().cpu().numpy(), ref, f"groups={groups}")
+    else:
+        rows = sample_rows(wl, gp.info["block_q"])
+        got = out[0, torch.from_numpy(rows).cuda()].float().cpu().numpy()
+        for h in range(wl.heads):
+            ref = oracle.attention_rows(q_np, k_np, v_np, wl.frames, wl.tokens_per_frame,
+                                        wl.window, 0, h, rows)
+            assert_close(got[:, h], ref, f"groups={groups} group {h // gp.geometry.heads} "
+                                         f"head {h}")
 
 
 @pytest.mark.parametrize("name", ["small", "720p"])
