@@ -40,6 +40,7 @@ extern "C" {
 #define SFA_ERR_UNSUPPORTED (-2) /* T % 16 != 0, head_dim not 64/128, misaligned data */
 #define SFA_ERR_HIP (-3)         /* HIP launch/runtime error (see sfa_status_str) */
 #define SFA_ERR_NOMEM (-4)       /* host allocation failed */
+#define SFA_ERR_TOO_LARGE (-5)   /* sfa_attention_static: workspace beyond its 64 MiB */
 
 /* Attention geometry. One plan per geometry (section "Workload and porting":
  * every attention is dispatched to a kernel shaped for it). */
@@ -190,6 +191,19 @@ int sfa_fwd(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v, sfa_
 /* sfa_norms followed by sfa_fwd. */
 int sfa_attention(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v,
                   sfa_tensor o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* sfa_attention without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is a fixed 64 MiB array in the library, one per GPU, held
+ * from the first call on that GPU until the process ends. The call allocates nothing.
+ * Plans whose workspace_bytes exceed 64 MiB get SFA_ERR_TOO_LARGE (e.g. 8 heads of d =
+ * 128 over S = 8192 tokens fit; the 720p-shaped layer does not). `stream` must run on the
+ * current device (SFA_ERR_INVALID otherwise). Every call on a GPU uses that GPU's one
+ * array, so calls that overlap on one GPU (other streams, other threads) race; calls
+ * ordered on one stream are safe, and nothing left in the array by an earlier call is
+ * read. */
+int sfa_attention_static(const sfa_plan* plan, sfa_tensor q, sfa_tensor k, sfa_tensor v,
+                         sfa_tensor o, void* stream);
 
 /* Head-group split (section "Hiding collectives": heads are independent and the
  * mask does not depend on them, so they can be processed in groups, each group

@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     Plan,
     attention,
     attention_groups,
+    attention_static,
     frame_stats,
     fwd,
     generic_attention,
@@ -21,6 +22,7 @@ from .api import (  # noqa: F401
     row_norms,
     sfa_attention,
     sfa_attention_groups,
+    sfa_attention_static,
     sfa_fwd,
     sfa_generic_attention,
     sfa_norms,

@@ -12,6 +12,7 @@ SFA_ERR_INVALID = -1
 SFA_ERR_UNSUPPORTED = -2
 SFA_ERR_HIP = -3
 SFA_ERR_NOMEM = -4
+SFA_ERR_TOO_LARGE = -5
 
 
 class Geometry(ctypes.Structure):
@@ -58,6 +59,7 @@ class PrologueGeometry(ctypes.Structure):
 EXPORTS = (
     "sfa_plan_create", "sfa_plan_create_ex", "sfa_plan_destroy", "sfa_plan_get_info",
     "sfa_plan_key_ranges", "sfa_plan_item", "sfa_plan_item_keys", "sfa_norms", "sfa_fwd", "sfa_attention",
+    "sfa_attention_static",
     "sfa_attention_groups", "sfa_read_head_stats", "sfa_read_row_norms", "sfa_read_frame_stats",
     "sfa_read_staged",
     "sfa_prologue_fold", "sfa_qkv_prologue",
@@ -93,6 +95,7 @@ def _declare(lib):
         "sfa_fwd": (ctypes.c_int, [P, Tensor, Tensor, Tensor, Tensor, P, ctypes.c_size_t, P]),
         "sfa_attention": (ctypes.c_int, [P, Tensor, Tensor, Tensor, Tensor, P, ctypes.c_size_t,
                                          P]),
+        "sfa_attention_static": (ctypes.c_int, [P, Tensor, Tensor, Tensor, Tensor, P]),
         "sfa_attention_groups": (ctypes.c_int, [P, ctypes.c_int32, Tensor, Tensor, Tensor, Tensor,
                                                 P, ctypes.c_size_t, P, ctypes.POINTER(P),
                                                 ctypes.c_int32]),

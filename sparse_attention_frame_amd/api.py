@@ -161,6 +161,20 @@ def sfa_attention(plan: Plan, q, k, v, out=None, workspace=None, stream=None):
     return out, ws
 
 
+def sfa_attention_static(plan: Plan, q, k, v, out=None, stream=None):
+    """sfa_attention on the library's fixed per-GPU workspace (no workspace argument, no
+    device allocation by the library; plans beyond its 64 MiB raise). Returns out."""
+    import torch
+
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    check(lib().sfa_attention_static(plan.handle, as_tensor(q, plan, "q"),
+                                     as_tensor(k, plan, "k"), as_tensor(v, plan, "v"),
+                                     as_tensor(out, plan, "o"), _stream_ptr(stream)),
+          "sfa_attention_static")
+    return out
+
+
 def sfa_attention_groups(group_plan: Plan, groups: int, q, k, v, out=None, workspace=None,
                          streams=(), stream=None):
     """sfa_attention on `groups` consecutive head groups of q, k, v ([B, S, groups*Hg, d]),
@@ -368,6 +382,7 @@ def sfa_generic_attention(plan: GenericPlan, q, k, v, out=None, workspace=None, 
 norms = sfa_norms
 fwd = sfa_fwd
 attention = sfa_attention
+attention_static = sfa_attention_static
 attention_groups = sfa_attention_groups
 head_stats = sfa_read_head_stats
 row_norms = sfa_read_row_norms

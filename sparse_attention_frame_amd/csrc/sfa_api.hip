@@ -11,13 +11,24 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "sfa_internal.h"
 
 using namespace sfa;
 
+// Workspace of sfa_attention_static: one copy on every GPU the library runs it on, held
+// until the process ends. Host code never uses this name as an address: it asks the
+// runtime for each device's copy (static_scratch below).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
 
 thread_local hipError_t g_last_hip = hipSuccess;
 thread_local char g_msg[256];
@@ -644,6 +655,34 @@ int sfa_attention(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v, s
   return sfa_fwd(p, q, k, v, o, ws, ws_bytes, stream);
 }
 
+int sfa_attention_static(const sfa_plan* p, sfa_tensor q, sfa_tensor k, sfa_tensor v,
+                         sfa_tensor o, void* stream) {
+  if (!p) return SFA_ERR_INVALID;
+  if (p->ws.total > kStaticScratchBytes) return SFA_ERR_TOO_LARGE;
+  // the stream must run on the current device: the scratch address is per device
+  int dev = 0, sdev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && stream) e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+  if (e != hipSuccess) return hip_status(e);
+  if (stream && sdev != dev) return SFA_ERR_INVALID;
+  if (dev < 0 || dev >= kMaxDevices) return SFA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  {
+    // first call on this device, with the device current: the address of its copy
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* ptr = nullptr;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      g_scratch_ptr[dev] = ptr;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  // sfa_norms writes every workspace array the attention kernel reads, the work-queue and
+  // split-item counters included, so nothing left by an earlier call is used
+  return sfa_attention(p, q, k, v, o, ws, kStaticScratchBytes, stream);
+}
+
 int sfa_attention_groups(const sfa_plan* p, int32_t groups, sfa_tensor q, sfa_tensor k,
                          sfa_tensor v, sfa_tensor o, void* ws, size_t ws_bytes, void* stream,
                          void* const* group_streams, int32_t nstreams) {
@@ -777,6 +816,9 @@ const char* sfa_status_str(int status) {
     case SFA_ERR_UNSUPPORTED:
       return "unsupported (T % 16 != 0, head_dim not 64/128, misaligned pointer or stride)";
     case SFA_ERR_NOMEM: return "host allocation failed";
+    case SFA_ERR_TOO_LARGE:
+      return "the plan needs more workspace than sfa_attention_static's fixed 64 MiB (use "
+             "sfa_attention with a caller-provided workspace)";
     case SFA_ERR_HIP:
       snprintf(g_msg, sizeof(g_msg), "HIP error %d: %s", int(g_last_hip),
                hipGetErrorString(g_last_hip));

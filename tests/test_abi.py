@@ -318,6 +318,17 @@ def test_read_calls_check_the_workspace_size(L):
     assert L.sfa_read_staged(None, ws, need, u16, u16, None) == _lib.SFA_ERR_INVALID
 
 
+def test_static_entry_refuses_before_any_launch(L):
+    """sfa_attention_static checks the plan against its fixed 64 MiB workspace before it
+    touches the GPU (this runs on CPU): the 720p-shaped layer needs more."""
+    p = Plan.for_workload(W.ALL["720p"])
+    assert p.info["workspace_bytes"] > 64 << 20
+    t = _lib.Tensor(4096, 1 << 12, 128, 0)
+    assert L.sfa_attention_static(p.handle, t, t, t, t, None) == _lib.SFA_ERR_TOO_LARGE
+    assert L.sfa_attention_static(None, t, t, t, t, None) == _lib.SFA_ERR_INVALID
+    assert b"64 MiB" in L.sfa_status_str(_lib.SFA_ERR_TOO_LARGE)
+
+
 def test_bound_limit_cap(L):
     """bound_limit above 126 / (2 log2 e) would let the largest weight of a row underflow
     on the fixed-maximum path; the plan refuses it (negative limits force the online
