@@ -8,7 +8,14 @@ roofline = the attention kernel alone (sfa_fwd is exactly one launch), timed
          with HIP events on its stream, against the bf16 dense MFMA peak;
          traffic = its HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
          (profiles/), null if the kernel source changed since.
-cpu_baseline = the fp64 CPU oracle on a bounded sample of the same layer.
+         measured_peak / pct_of_measured_peak = the same rate against chains of
+         v_mfma_f32_32x32x16_bf16 with no memory traffic, timed live (libsfa_probe.so);
+         loop_ceiling = the attention tile loop with its operands already in LDS (no
+         HBM, no barriers), timed live: what this loop design can reach on the chip;
+         sustained_clock_ghz = GRBM_GUI_ACTIVE cycles per XCD / kernel time from the
+         committed rocprofv3 counters (profiles/), null if the kernel changed since.
+cpu_baseline = the fp64 CPU oracle on a bounded sample of the same layer, one query frame
+         of one head per task over a pool of host threads.
 """
 import argparse
 import json
@@ -26,6 +33,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_720p_traffic.json")
 KERNEL_SOURCES = ("sparse_attention_frame_amd/csrc/sfa_attn.h",
                   "sparse_attention_frame_amd/csrc/sfa_fwd.hip",
                   "sparse_attention_frame_amd/csrc/sfa_internal.h")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_720p_clock.json")
 PRO_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prologue_kernel_720p_traffic.json")
 PRO_SOURCES = ("sparse_attention_frame_amd/csrc/sfa_attn.h",
                "sparse_attention_frame_amd/csrc/sfa_prologue.hip",
@@ -42,16 +50,34 @@ def kernel_source_hash(sources=KERNEL_SOURCES):
     return h.hexdigest()
 
 
-def measured_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
-    """HBM bytes per kernel launch from the committed rocprofv3 counters, or None when
-    the kernel source changed since they were taken."""
+def measured_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES, key="bytes_per_launch"):
+    """A figure of the committed rocprofv3 counters (HBM bytes per kernel launch by
+    default), or None when the kernel source changed since they were taken."""
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     if t.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
-    return t.get("bytes_per_launch")
+    return t.get(key)
+
+
+def probe_ceilings():
+    """Live matrix-core microbenchmarks (libsfa_probe.so), 8 waves per CU as the attention
+    kernel runs: the MFMA-chain peak and the tile-loop ceilings, each the best of three
+    launches. clock_ghz is the probe's own shader clock (s_memtime over s_memrealtime)."""
+    from sparse_attention_frame_amd import probe
+
+    out = {}
+    for name, kind, iters in (("mfma_chain", probe.MFMA_CHAIN, 80000),
+                              ("tile_loop_32rows", probe.TILE_LOOP, 40000),
+                              ("tile_loop_64rows", probe.TILE_LOOP64, 20000),
+                              ("tile_loop_32rows_no_softmax", probe.TILE_NOEXP, 40000)):
+        r = max((probe.run(kind, waves=8, iters=iters) for _ in range(3)),
+                key=lambda x: x["tflops"])   # best of three launches
+        out[name] = {"tflops": round(r["tflops"], 1), "frac": round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "clock_ghz": round(r["clock_ghz"], 3), "mfma_busy": round(r["mfma_busy"], 3)}
+    return out
 
 
 def log(msg):
@@ -69,44 +95,76 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(wl, q_np, k_np, v_np, out_head0=None, gpu_stats=None, budget_s=12.0,
-                 bound_limit=40.0):
-    """Time the oracle (as it stands) on whole query frames of head 0 until ~budget_s. With
-    the GPU output of head 0 ([S, d] float32) it also reports the parity of those rows, and
-    with the GPU's per-head statistics whether the eligibility flags match the oracle's."""
+def host_workers():
+    """Threads for the CPU baseline: the cores this process may run on, capped by
+    OMP_NUM_THREADS when set (a shared host grants one job a share of its cores)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_baseline(wl, q_np, k_np, v_np, out_gpu=None, gpu_stats=None, budget_s=12.0,
+                 bound_limit=40.0, block=1024):
+    """Time the oracle (as it stands) on blocks of up to `block` query rows inside one
+    query frame (oracle.attention_block), one (batch, head, block) per task over a pool of
+    host threads with one BLAS thread each, until about budget_s. With the GPU output
+    ([B, S, H, d] float32) it also reports the parity of the rows done, and with the GPU's
+    per-head statistics whether the eligibility flags match the oracle's."""
+    import threading
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
     T, F, d = wl.tokens_per_frame, wl.frames, wl.head_dim
-    order = [F // 2] + [f for f in range(F + 1) if f != F // 2]   # a full-window frame first
-    flops = 0.0
+    workers = host_workers()
+    frames = [F // 2] + [f for f in range(F + 1) if f != F // 2]   # a full-window frame first
+    tasks = [(b, h, r0, min(r0 + block, (f + 1) * T)) for b in range(wl.batch)
+             for h in range(wl.heads) for f in frames for r0 in range(f * T, (f + 1) * T, block)]
+    lock = threading.Lock()
+    heads = {}
     done = []
-    refs = []
     t0 = time.perf_counter()
-    for f in order:
-        rows = np.arange(f * T, (f + 1) * T)
-        refs.append((rows, oracle.attention_rows(q_np, k_np, v_np, F, T, wl.window, 0, 0, rows)))
-        nkeys = len(oracle.key_frames(f, F, wl.window)) * T
-        flops += 4.0 * d * T * nkeys
-        done.append(f)
+
+    def one(task):
         if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            return
+        b, h, r0, r1 = task
+        with lock:
+            if (b, h) not in heads:
+                heads[(b, h)] = tuple(np.ascontiguousarray(x[b, :, h, :], dtype=np.float64)
+                                      for x in (q_np, k_np, v_np))
+            qh, kh, vh = heads[(b, h)]
+        ref = oracle.attention_block(qh, kh, vh, F, T, wl.window, r0, r1)
+        with lock:
+            done.append((task, ref, time.perf_counter()))
+
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, tasks))
+    if not done:
+        return None
+    dt = max(t for *_, t in done) - t0
+    flops = sum(4.0 * d * (r1 - r0) * len(oracle.key_frames(r0 // T, F, wl.window)) * T
+                for (_, _, r0, r1), *_ in done)
+    rows = sum(r1 - r0 for (_, _, r0, r1), *_ in done)
+    hs = sorted({(b, h) for (b, h, _, _), *_ in done})
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
            "kind": "oracle", "cpu": cpu_model(),
-           "sample": f"head 0, query frames {done} ({len(done) * T} rows) of the {wl.name} layer, "
-                     f"fp64 dense-masked numpy, {dt:.1f} s"}
-    if out_head0 is not None:
+           "sample": f"{len(done)} blocks of <= {block} query rows ({rows} rows) of (batch, head) "
+                     f"{hs} of the {wl.name} layer, frame {F // 2} first, fp64 dense-masked "
+                     f"numpy on {workers} threads, {dt:.1f} s"}
+    if out_gpu is not None:
         # parity of the same rows in the same run (tolerance: max-abs 2e-2, rel-L2 5e-3)
-        got = np.concatenate([out_head0[r] for r, _ in refs]).astype(np.float64)
-        ref = np.concatenate([o for _, o in refs])
-        diff = got - ref
+        got = np.concatenate([out_gpu[b, r0:r1, h] for (b, h, r0, r1), _, _ in done])
+        ref = np.concatenate([r for _, r, _ in done])
+        diff = got.astype(np.float64) - ref
         res["parity"] = {"rows": int(len(ref)), "max_abs": float(np.abs(diff).max()),
                          "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(ref)),
                          "pass": bool(np.abs(diff).max() <= 2e-2
@@ -280,6 +338,8 @@ def main():
     ap.add_argument("--prologue", action="store_true",
                     help="time the fused q/k/v prologue (RMSNorm, projection, rotary, packing) "
                          "at the 720p layer's shape instead of the attention")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the live matrix-core microbenchmarks (measured peak, loop ceiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one elementwise copy of this size (calibrates HBM counters)")
     args = ap.parse_args()
@@ -377,6 +437,10 @@ def main():
     assert torch.isfinite(out.float()).all(), "non-finite output"
 
     traffic = measured_traffic()
+    default_launch = (G == 1 and args.bound_mode == 0 and wl.name == "720p"
+                      and args.bound_limit == 40.0 and args.ablation == "none"
+                      and not (args.waves or args.block_q or args.lds_stages or args.key_split
+                               or args.wave_rows))
 
     res = {
         "metric": METRIC,
@@ -416,12 +480,27 @@ def main():
                                 else "fwd_kernel" if G == 1 else f"whole step ({G} head groups)"),
                      "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": (traffic if G == 1 and args.bound_mode == 0
-                                 and wl.name == "720p" and args.bound_limit == 40.0
-                                 and not (args.waves or args.block_q or args.lds_stages or args.key_split
-                                          or args.wave_rows)
-                                 and args.ablation == "none" else None)},
+                     "traffic": traffic if default_launch else None,
+                     "sustained_clock_ghz": (measured_traffic(CLOCK_FILE, key="clock_ghz")
+                                             if default_launch else None)},
     }
+    if wl.window >= wl.frames:
+        # every video frame sees every frame: compare with dense attention over all S keys
+        dense = 4.0 * wl.head_dim * float(wl.seq) ** 2 * wl.heads * wl.batch
+        res["dense"] = {"gflop": round(dense / 1e9, 1),
+                        "tflops_equiv": round(dense / (fwd_ms * 1e-3) / 1e12, 2),
+                        "frac_of_peak": round(dense / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "note": "dense 4*d*S^2*H*B flops over the attention kernel's time"}
+    if not args.no_probe:
+        log("bench: matrix-core microbenchmarks")
+        ceil = probe_ceilings()
+        rf = res["roofline"]
+        rf["measured_peak"] = {**ceil["mfma_chain"],
+                               "probe": "independent v_mfma_f32_32x32x16_bf16 chains, 8 waves "
+                                        "per CU, no memory (libsfa_probe.so)"}
+        rf["pct_of_measured_peak"] = round(100.0 * fwd_tf / ceil["mfma_chain"]["tflops"], 2)
+        rf["loop_ceiling"] = {k: v for k, v in ceil.items() if k != "mfma_chain"}
+        rf["pct_of_loop_ceiling"] = round(100.0 * fwd_tf / ceil["tile_loop_32rows"]["tflops"], 2)
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 2
         x = torch.ones(n, dtype=torch.bfloat16, device=dev)
@@ -431,8 +510,7 @@ def main():
         res["copy_probe_mib"] = args.copy_probe_mib
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(wl, q_np, k_np, v_np,
-                                           out[0, :, 0].float().cpu().numpy(), st,
+        res["cpu_baseline"] = cpu_baseline(wl, q_np, k_np, v_np, out.float().cpu().numpy(), st,
                                            bound_limit=args.bound_limit)
     print(json.dumps(res), flush=True)
 

@@ -1,4 +1,5 @@
-"""Build libsfa.so (host planner + gfx950 kernels + C ABI) with hipcc, in-tree."""
+"""Build libsfa.so (host planner + gfx950 kernels + C ABI) and libsfa_probe.so (the
+matrix-core microbenchmarks the benchmark compares against) with hipcc, in-tree."""
 from __future__ import annotations
 
 import glob
@@ -11,6 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsfa.so")
+PROBE_LIB = os.path.join(PKG, "libsfa_probe.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [
@@ -39,6 +41,10 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
+def probe_sources():
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "probe", "*.hip")))
+
+
 # the host pass warns that it does not know the packed-fp32 feature: harmless
 _NOISE = "is not a recognized feature for this target"
 
@@ -55,23 +61,27 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into sparse_attention_frame_amd/libsfa.so (always rebuilds)."""
+    """Compile every source into sparse_attention_frame_amd/libsfa.so and the probes into
+    libsfa_probe.so (always rebuilds). Returns the path of libsfa.so."""
     os.makedirs(OBJ_DIR, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+    targets = {LIB: [], PROBE_LIB: []}
     jobs = []
-    for src in sources():
-        name = os.path.basename(src)
-        obj = os.path.join(OBJ_DIR, name + ".o")
-        jobs.append((obj, [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(name, []), *inc, "-c", src,
-                           "-o", obj]))
+    for lib, srcs in ((LIB, sources()), (PROBE_LIB, probe_sources())):
+        for src in srcs:
+            name = os.path.basename(src)
+            obj = os.path.join(OBJ_DIR, name + ".o")
+            targets[lib].append(obj)
+            jobs.append([hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(name, []), *inc, "-c", src,
+                         "-o", obj])
     workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
     with ThreadPoolExecutor(workers) as ex:
-        for f in [ex.submit(_run, cmd, verbose) for _, cmd in jobs]:
+        for f in [ex.submit(_run, cmd, verbose) for cmd in jobs]:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp],
-         verbose)
-    os.replace(tmp, LIB)
+    for lib, objs in targets.items():
+        tmp = lib + ".tmp"
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

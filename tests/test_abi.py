@@ -46,6 +46,26 @@ def test_every_declared_symbol_is_exported(L):
     assert set(declared) <= exported
 
 
+def test_probe_library_exports_its_header():
+    """libsfa_probe.so (the microbenchmarks the benchmark reports against) exports what
+    include/sfa_probe.h declares; the calls need a GPU and are not made here."""
+    from sparse_attention_frame_amd import probe
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "sfa_probe.h")).read(),
+                  flags=re.S)
+    declared = sorted(set(re.findall(r"\b(sfa_[a-z_]+)\s*\(", text)))
+    assert declared == sorted(probe.EXPORTS)
+    pl = probe.lib()
+    assert pl.sfa_probe_scratch_bytes() >= 1024 * 512 * 4
+    out = subprocess.run(["nm", "-D", "--defined-only", probe.PROBE_LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    assert set(declared) <= set(re.findall(r"\bT (sfa_[a-z_]+)\b", out))
+    r = probe.Result()
+    # argument checks come before any HIP call
+    assert pl.sfa_probe_run(9, 8, 10, None, 0, None, r) == -1
+    assert pl.sfa_probe_run(0, 6, 10, None, 0, None, r) == -1
+
+
 def test_status_strings(L):
     for st in (0, -1, -2, -3, -4):
         assert L.sfa_status_str(st)

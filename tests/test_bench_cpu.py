@@ -43,16 +43,26 @@ def test_traffic_records_are_well_formed(path, sources):
 def test_cpu_baseline_parity_and_eligibility_checks():
     wl = W.TINY
     q, k, v = W.make_inputs_np(wl)
-    ref = oracle.attention(q, k, v, wl.frames, wl.tokens_per_frame, wl.window)[0, :, 0]
+    ref = oracle.attention(q, k, v, wl.frames, wl.tokens_per_frame, wl.window)
     flags = oracle.head_stats(q, k)["eligible"]
     good = bench.cpu_baseline(wl, q, k, v, ref.astype(np.float32), {"eligible": flags},
-                              budget_s=0.2)
+                              budget_s=5.0)
     assert good["kind"] == "oracle" and good["value"] > 0
+    assert good["cores"] == bench.host_workers() >= 1
+    # every (batch, head, frame) of the tiny layer fits the budget
+    assert good["parity"]["rows"] == wl.batch * wl.heads * wl.seq
     assert good["parity"]["pass"] and good["eligibility_match"]
     bad_out = ref.astype(np.float32).copy()
-    bad_out[5, 3] += 0.1
-    bad = bench.cpu_baseline(wl, q, k, v, bad_out, {"eligible": ~flags}, budget_s=0.2)
+    bad_out[0, (wl.frames // 2) * wl.tokens_per_frame + 5, 1, 3] += 0.1   # first frame timed
+    bad = bench.cpu_baseline(wl, q, k, v, bad_out, {"eligible": ~flags}, budget_s=5.0)
     assert not bad["parity"]["pass"] and not bad["eligibility_match"]
+
+
+def test_host_workers_honours_the_thread_cap(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert bench.host_workers() == min(3, len(os.sched_getaffinity(0)))
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.host_workers() == len(os.sched_getaffinity(0))
 
 
 def test_cpu_baseline_prologue_parity_check():
