@@ -5,7 +5,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsfa.so")
+# SFA_LIBRARY names another build of the same library (the sanitizer build of the host
+# code that the CPU tests load); by default the in-tree libsfa.so
+LIB_PATH = os.environ.get("SFA_LIBRARY") or os.path.join(_HERE, "libsfa.so")
 
 SFA_OK = 0
 SFA_ERR_INVALID = -1

@@ -85,5 +85,47 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(OBJ_DIR, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libsfa_san.so")
+# host code under AddressSanitizer and UndefinedBehaviorSanitizer (each -fsanitize= goes to
+# the host pass only); the device code is built as usual, at -O1 to build quickly
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-g", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The shared ASan runtime of hipcc's clang (preloaded into the Python process that
+    loads the sanitizer build)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    res = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True)
+    path = res.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the clang ASan runtime was not found")
+    return path
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Build the library with the host code (planner, validation, C ABI) instrumented by
+    ASan and UBSan into _build/san/libsfa_san.so, for the CPU tests; not for GPU runs."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+    flags = [f if f != "-O3" else "-O1" for f in HIPCC_FLAGS] + SAN_FLAGS
+    objs, jobs = [], []
+    for src in sources():
+        obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+        objs.append(obj)
+        jobs.append([hipcc(), *flags, *inc, "-c", src, "-o", obj])
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(workers) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for cmd in jobs]:
+            f.result()
+    tmp = SAN_LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+          "-Xarch_host", "-fsanitize=undefined", *objs, "-o", tmp], verbose)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
