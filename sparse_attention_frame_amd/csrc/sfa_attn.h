@@ -84,6 +84,14 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// The larger of a lane's value and that of lane ^ 32 (the other key half of the same
+// query row): one v_permlane32_swap, no LDS round trip.
+__device__ inline float max_xor32(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, uint32_t(r[0])), __builtin_bit_cast(float, uint32_t(r[1])));
+}
+
 // Wait until at most N of this wave's vector-memory operations (the LDS DMAs
 // of younger stages) are still in flight.
 template <int N>
@@ -241,7 +249,7 @@ struct Attn {
         float mx = s[t][0];
 #pragma unroll
         for (int i = 1; i < NV; ++i) mx = fmaxf(mx, s[t][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cexp;
+        mx = max_xor32(mx) * cexp;
         // lazy rescale: keep the stale maximum while the tile stays within 2^kLazy
         // of it (exact up to rounding: numerator and denominator share the shift)
         const bool grow = mx > mrow[t] + kLazy;
@@ -322,6 +330,30 @@ struct Attn {
       l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), kOnes, l, false);
     }
   }
+  // Online numerators of one tile for the pipelined loop. The running maximum is lazy per
+  // row and branch-free: a row whose tile maximum exceeds it by more than kLazy takes the
+  // tile maximum, the others keep theirs (alpha = exp2(0) = 1). The row sum is rescaled
+  // here; the returned alpha rescales the row's O once the PV of the previous tile, which
+  // is still relative to the old maximum, has been added.
+  __device__ static inline float softmax_online(const f32x16& s, float& m, float& l,
+                                                uint32_t (&pk)[8], float cexp) {
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = max_xor32(mx) * cexp;
+    const float mnew = mx > m + kLazy ? mx : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    l *= alpha;
+    softmax_fixed(s, m, l, pk, cexp);
+    return alpha;
+  }
+  __device__ static inline void rescale(f32x16 (&o)[DT], float alpha) {
+    if (__ballot(alpha != 1.0f) != 0) {  // rare: a row moved its maximum
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+  }
   __device__ static inline void pv(const VFrag& f, const uint32_t (&pk)[8], f32x16 (&o)[DT]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -335,13 +367,14 @@ struct Attn {
   // Region with V^T one region ahead: the 8 K reads of QK(j+1) first, then the 16 MFMAs
   // with 3 VALU ops behind each, and the 8 reads of the next tile's V^T operand placed
   // after the PV MFMAs that consume the same registers.
+  template <int VALU>
   __device__ static inline void interleave_kv() {
     __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // DS read: K
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       if (i >= 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read: V^T
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);  // VALU
     }
   }
 
@@ -400,9 +433,11 @@ struct Attn {
     const int nfull = ngran / GPS;
     const int rem = ngran - nfull * GPS;
     const int nst = nfull + (rem > 0 ? 1 : 0);
-    if constexpr (!ONLINE && NT == 1 && TPS == 2 && (NBUF == 3 || NBUF == 4)) {
+    if constexpr (NT == 1 && TPS == 2 && (NBUF == 3 || NBUF == 4)) {
       // Tile-level software pipeline over the N = 2*nfull full 32-key tiles:
-      //   region j:  QK(j+1) + PV(j-1)  (16 MFMAs)  ||  softmax(j)  (48 VALU)
+      //   region j:  QK(j+1) + PV(j-1)  (16 MFMAs)  ||  softmax(j)  (48 VALU, about 70
+      //   with the online maximum, whose O rescale, if any row moved its maximum, follows
+      //   the region's PV)
       // Region j reads K(j+1) for its own QK and V^T(j) for the PV of region j+1,
       // so the V^T reads have a whole region to land. Stage s (tiles 2s, 2s+1)
       // sits in buffer s % NBUF; barrier B_s, just before the region that first
@@ -449,7 +484,10 @@ struct Attn {
         load_k(kf, lds, L, 2 * GB);
         f32x16 snext = qk(kf, qf[0]);
         load_v(vf, lds, L, 0);  // V^T(0), used by PV(0) in region 1
-        softmax_fixed(scur, mrow[0], lsum[0], pprev, p.c);
+        if constexpr (ONLINE)
+          softmax_online(scur, mrow[0], lsum[0], pprev, p.c);  // O is still zero
+        else
+          softmax_fixed(scur, mrow[0], lsum[0], pprev, p.c);
         scur = snext;
         __builtin_amdgcn_sched_barrier(0);
         // steady regions j = 1 .. N-2, unrolled over the 2*NBUF-tile period of (buffer, half)
@@ -473,8 +511,15 @@ struct Attn {
             snext = qk(kf, qf[0]);
             pv(vf, pprev, oo);                                 // V^T(j-1), read last region
             load_v(vf, lds, L, bc * STAGE_B + tc * 2 * GB);  // V^T(j) for the next region
-            softmax_fixed(scur, mrow[0], lsum[0], pcur, p.c);
-            interleave_kv();
+            if constexpr (ONLINE) {
+              const float alpha = softmax_online(scur, mrow[0], lsum[0], pcur, p.c);
+              interleave_kv<4>();
+              __builtin_amdgcn_sched_barrier(0);
+              rescale(oo, alpha);
+            } else {
+              softmax_fixed(scur, mrow[0], lsum[0], pcur, p.c);
+              interleave_kv<3>();
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 8; ++i) pprev[i] = pcur[i];
@@ -486,7 +531,10 @@ struct Attn {
           const int jm = N - 2;  // tiles N-2 and N-1 are the two halves of stage nfull-1
           const int b = ((jm / 2) % NBUF);
           pv(vf, pprev, oo);     // V^T(N-2), read in region N-2
-          softmax_fixed(scur, mrow[0], lsum[0], pcur, p.c);
+          if constexpr (ONLINE)
+            rescale(oo, softmax_online(scur, mrow[0], lsum[0], pcur, p.c));
+          else
+            softmax_fixed(scur, mrow[0], lsum[0], pcur, p.c);
           load_v(vf, lds, L, b * STAGE_B + 2 * GB);
           pv(vf, pcur, oo);
         }
