@@ -320,14 +320,17 @@ struct Attn {
     for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks], q[ks], s, 0, 0, 0);
     return s;
   }
-  __device__ static inline void softmax_fixed(const f32x16& s, float m, float& l, uint32_t (&pk)[8],
-                                              float cexp) {
+  // Numerators and their row sum, which two accumulators split (even and odd pairs) so
+  // that the chain of dependent dot2 operations is half as long.
+  __device__ static inline void softmax_fixed(const f32x16& s, float m, float& l, float& l2,
+                                              uint32_t (&pk)[8], float cexp) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * i], cexp, -m));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * i + 1], cexp, -m));
       pk[i] = pack_bf16x2(p0, p1);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), kOnes, l, false);
+      float& acc = (i & 1) ? l2 : l;
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), kOnes, acc, false);
     }
   }
   // Online numerators of one tile for the pipelined loop. The running maximum is lazy per
@@ -335,7 +338,7 @@ struct Attn {
   // tile maximum, the others keep theirs (alpha = exp2(0) = 1). The row sum is rescaled
   // here; the returned alpha rescales the row's O once the PV of the previous tile, which
   // is still relative to the old maximum, has been added.
-  __device__ static inline float softmax_online(const f32x16& s, float& m, float& l,
+  __device__ static inline float softmax_online(const f32x16& s, float& m, float& l, float& l2,
                                                 uint32_t (&pk)[8], float cexp) {
     float mx = s[0];
 #pragma unroll
@@ -345,7 +348,8 @@ struct Attn {
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
     l *= alpha;
-    softmax_fixed(s, m, l, pk, cexp);
+    l2 *= alpha;
+    softmax_fixed(s, m, l, l2, pk, cexp);
     return alpha;
   }
   __device__ static inline void rescale(f32x16 (&o)[DT], float alpha) {
@@ -477,6 +481,7 @@ struct Attn {
         KFrag kf;
         VFrag vf;
         uint32_t pprev[8], pcur[8];
+        float l2 = 0.f;  // second row-sum accumulator
         load_k(kf, lds, L, 0);
         f32x16 scur = qk(kf, qf[0]);
         // region 0: QK(1) + softmax(0)
@@ -485,9 +490,9 @@ struct Attn {
         f32x16 snext = qk(kf, qf[0]);
         load_v(vf, lds, L, 0);  // V^T(0), used by PV(0) in region 1
         if constexpr (ONLINE)
-          softmax_online(scur, mrow[0], lsum[0], pprev, p.c);  // O is still zero
+          softmax_online(scur, mrow[0], lsum[0], l2, pprev, p.c);  // O is still zero
         else
-          softmax_fixed(scur, mrow[0], lsum[0], pprev, p.c);
+          softmax_fixed(scur, mrow[0], lsum[0], l2, pprev, p.c);
         scur = snext;
         __builtin_amdgcn_sched_barrier(0);
         // steady regions j = 1 .. N-2, unrolled over the 2*NBUF-tile period of (buffer, half)
@@ -512,12 +517,12 @@ struct Attn {
             pv(vf, pprev, oo);                                 // V^T(j-1), read last region
             load_v(vf, lds, L, bc * STAGE_B + tc * 2 * GB);  // V^T(j) for the next region
             if constexpr (ONLINE) {
-              const float alpha = softmax_online(scur, mrow[0], lsum[0], pcur, p.c);
+              const float alpha = softmax_online(scur, mrow[0], lsum[0], l2, pcur, p.c);
               interleave_kv<4>();
               __builtin_amdgcn_sched_barrier(0);
               rescale(oo, alpha);
             } else {
-              softmax_fixed(scur, mrow[0], lsum[0], pcur, p.c);
+              softmax_fixed(scur, mrow[0], lsum[0], l2, pcur, p.c);
               interleave_kv<3>();
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -532,12 +537,13 @@ struct Attn {
           const int b = ((jm / 2) % NBUF);
           pv(vf, pprev, oo);     // V^T(N-2), read in region N-2
           if constexpr (ONLINE)
-            rescale(oo, softmax_online(scur, mrow[0], lsum[0], pcur, p.c));
+            rescale(oo, softmax_online(scur, mrow[0], lsum[0], l2, pcur, p.c));
           else
-            softmax_fixed(scur, mrow[0], lsum[0], pcur, p.c);
+            softmax_fixed(scur, mrow[0], lsum[0], l2, pcur, p.c);
           load_v(vf, lds, L, b * STAGE_B + 2 * GB);
           pv(vf, pcur, oo);
         }
+        lsum[0] += l2;
       } else if (nst > 0) {
         issue_stage(lds, 0, L, W, X, 0, rem);
       }
