@@ -31,13 +31,24 @@ def test_traffic_records_are_well_formed(path, sources):
         t = json.load(f)
     assert t["bytes_per_launch"] >= t["algorithmic_min_bytes"] > 0
     assert len(t["kernel_source_sha256"]) == 64
-    assert all(c.startswith("rocprofv3 --pmc ") for c in t["commands"])
+    assert all("rocprofv3 --pmc " in c and "bench.py" in c for c in t["commands"])
     # the FETCH_SIZE / WRITE_SIZE scales come from the copy probe of 1024 MiB (4 decimals)
     assert abs(t["fetch_scale"] * t["copy_fetch_kib"] / 1048576 - 1) < 1e-3
     assert abs(t["write_scale"] * t["copy_write_kib"] / 1048576 - 1) < 1e-3
     # bench reports the record only while the sources are the ones it was taken on
     current = bench.measured_traffic(path, sources)
     assert current in (None, t["bytes_per_launch"])
+
+
+def test_clock_record_is_well_formed():
+    with open(bench.CLOCK_FILE) as f:
+        c = json.load(f)
+    assert "GRBM_GUI_ACTIVE" in c["command"] and "rocprofv3 --pmc" in c["command"]
+    assert abs(c["gui_cycles_per_xcd"] * c["xcds"] - c["grbm_gui_active_total"]) < 1.0
+    # the clock is the cycles per XCD over the plain run's kernel time, below the 2.4 GHz peak
+    assert abs(c["clock_ghz"] - c["gui_cycles_per_xcd"] / c["trace_average_ns"]) < 1e-3
+    assert 0.5 < c["clock_ghz"] <= 2.4
+    assert bench.measured_traffic(bench.CLOCK_FILE, key="clock_ghz") in (None, c["clock_ghz"])
 
 
 def test_cpu_baseline_parity_and_eligibility_checks():
