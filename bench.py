@@ -14,8 +14,8 @@ roofline = the attention kernel alone (sfa_fwd is exactly one launch), timed
          HBM, no barriers), timed live: what this loop design can reach on the chip;
          sustained_clock_ghz = GRBM_GUI_ACTIVE cycles per XCD / kernel time from the
          committed rocprofv3 counters (profiles/), null if the kernel changed since.
-cpu_baseline = the fp64 CPU oracle on a bounded sample of the same layer, one query frame
-         of one head per task over a pool of host threads.
+cpu_baseline = the fp64 CPU oracle on a bounded sample of the same layer, blocks of up to
+         1024 query rows of one (batch, head) per task over a pool of host threads.
 """
 import argparse
 import json
@@ -41,12 +41,18 @@ PRO_SOURCES = ("sparse_attention_frame_amd/csrc/sfa_attn.h",
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES):
+    """sha256 of the kernel sources' code: comments and blank space are dropped first, so
+    a change to the comments alone leaves the profile records valid."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for rel in sources:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -42,14 +42,13 @@
 //     16-byte LDS load per lane; the O accumulator lane again holds one query
 //     row, so the online rescale and the final 1/l are per-lane scalars.
 //
-// Staging: the memory-bound prologue (sfa_norms) writes V^T [b][h][d][S] into
-// the workspace (LDS transpose reads run at well under half the rate of plain
-// 16-byte reads on gfx950). K rows and V^T granules then go from HBM straight into LDS by
-// DMA (buffer_load_dwordx4 ... lds: no registers, no VALU), in NBUF rotating 64-key
-// stages. 16-byte chunks are XOR-swizzled through the DMA source address
-// so the operand reads are free of bank conflicts:
-//   K   [key][d]            : chunk ^= key % 16 (16 lanes read 16 rows);
-//   V^T [granule][d][16 keys]: half ^= (d / 8) % 2 (16 lanes read 16 rows of 32 B).
+// Staging: the memory-bound prologue (sfa_norms) copies K and V into the workspace in
+// the byte order of the LDS stages (sfa_internal.h: K as [granule][16-byte chunk][16 keys],
+// V transposed as [granule][d][16 keys] with the halves of odd 8-row groups swapped, since
+// LDS transpose reads run at well under half the rate of plain 16-byte reads on gfx950).
+// Granules then go from HBM straight into LDS by DMA (buffer_load_dwordx4 ... lds: no
+// registers, no VALU), 1 KB of contiguous bytes per request, in NBUF rotating 64-key stages;
+// 16 lanes reading one operand hit 16 distinct 16-byte bank groups.
 #include "sfa_internal.h"
 
 namespace {
