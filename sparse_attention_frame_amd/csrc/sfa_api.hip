@@ -73,14 +73,21 @@ constexpr int kTargetItems = 256;
 // of 32 rows), or the whole frame when it is shorter. The last block of a frame takes
 // the remaining rows, so a frame costs ceil(T / 32) wave tiles, the fewest possible
 // (a block size that divides T, such as 240 rows for T = 3600, leaves 16 repeated
-// rows in the last wave tile of every block). When that gives fewer work items than
-// compute units (small layers), the block is the largest one that gives every compute
-// unit an item, but not less than one wave's rows.
-int auto_block_granules(int t_granules, int max_granules, int min_granules, int64_t groups) {
+// rows in the last wave tile of every block). When those blocks give fewer work items
+// than compute units (small layers), each frame is cut into the most blocks that still
+// give every compute unit at most one item, of balanced size, but not less than one
+// wave's rows: a block's time falls less than its rows do (its keys stream at a rate
+// of their own), so a second round of items costs more than larger blocks.
+// slots = work items per query block index (batch x heads x frame slots, a split frame
+// counting twice).
+int auto_block_granules(int t_granules, int max_granules, int min_granules, int64_t slots) {
   const int top = t_granules < max_granules ? t_granules : max_granules;
-  for (int gq = top; gq >= min_granules; --gq)
-    if (groups * ((t_granules + gq - 1) / gq) >= kTargetItems) return gq;
-  return top < min_granules ? top : min_granules;
+  if (top <= min_granules) return top;
+  if (slots * ((t_granules + top - 1) / top) >= kTargetItems) return top;
+  const int64_t nqb = kTargetItems / slots;  // >= 1 here
+  int64_t gq = (t_granules + nqb - 1) / nqb;
+  if (gq < min_granules) gq = min_granules;
+  return gq > top ? top : int(gq);
 }
 
 int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out) {
@@ -105,32 +112,7 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   if (bound_mode != 0 && bound_mode != 1) return SFA_ERR_UNSUPPORTED;
   const int key_split = opt ? opt->key_split : 0;
   if (key_split != 0 && key_split != -1) return SFA_ERR_UNSUPPORTED;
-  int gq;
-  if (block_q == 0) {
-    gq = auto_block_granules(tg, max_granules, wave_rows / kGranule,
-                             int64_t(geom->batch) * geom->heads * (geom->frames + 1));
-  } else {
-    if (block_q < 0 || block_q % kGranule != 0 || block_q / kGranule > max_granules)
-      return SFA_ERR_UNSUPPORTED;
-    gq = block_q / kGranule;
-    if (gq > tg) gq = tg;  // one block holds the whole frame
-  }
-  sfa_plan* p = new (std::nothrow) sfa_plan;
-  if (!p) return SFA_ERR_NOMEM;
-  memset(p, 0, sizeof(*p));
-  p->g = *geom;
   const int F = geom->frames, w = geom->window, B = geom->batch, H = geom->heads;
-  const int D = geom->head_dim;
-  p->scale = geom->scale == 0.0f ? 1.0f / sqrtf(float(D)) : geom->scale;
-  p->S = (F + 1) * T;
-  p->gq = gq;
-  p->waves = waves;
-  p->qt = qt;
-  p->stages = stages;
-  p->bound_mode = bound_mode;
-  p->nqb = (tg + gq - 1) / gq;  // the last block of a frame may be shorter
-  p->nchunk = (p->S + kNormChunk - 1) / kNormChunk;
-
   // Key split of the tail: the items of the cheapest query frames that see more than
   // one frame are the last multi-frame items the largest-first order starts, and the
   // longest of the short items that end the launch; each is split into two key halves
@@ -146,6 +128,31 @@ int create(const sfa_geometry* geom, const sfa_plan_options* opt, sfa_plan** out
   if (vmin > 0)
     for (int f = 1; f <= F; ++f) nsplit += visible_frames(f, F, w) == vmin;
   if (nsplit > kMaxSplitFrames || F + 1 + nsplit > kMaxFrameSlots) nsplit = 0;
+  int gq;
+  if (block_q == 0) {
+    gq = auto_block_granules(tg, max_granules, wave_rows / kGranule,
+                             int64_t(B) * H * (F + 1 + nsplit));
+  } else {
+    if (block_q < 0 || block_q % kGranule != 0 || block_q / kGranule > max_granules)
+      return SFA_ERR_UNSUPPORTED;
+    gq = block_q / kGranule;
+    if (gq > tg) gq = tg;  // one block holds the whole frame
+  }
+  sfa_plan* p = new (std::nothrow) sfa_plan;
+  if (!p) return SFA_ERR_NOMEM;
+  memset(p, 0, sizeof(*p));
+  p->g = *geom;
+  const int D = geom->head_dim;
+  p->scale = geom->scale == 0.0f ? 1.0f / sqrtf(float(D)) : geom->scale;
+  p->S = (F + 1) * T;
+  p->gq = gq;
+  p->waves = waves;
+  p->qt = qt;
+  p->stages = stages;
+  p->bound_mode = bound_mode;
+  p->nqb = (tg + gq - 1) / gq;  // the last block of a frame may be shorter
+  p->nchunk = (p->S + kNormChunk - 1) / kNormChunk;
+
   // slots: every query frame once, a split one as two halves; by decreasing cost (number
   // of visible frames of the slot), ties in slot order
   int cost[kMaxFrameSlots];

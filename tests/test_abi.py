@@ -72,25 +72,30 @@ def test_status_strings(L):
     assert b"unknown" in L.sfa_status_str(7)
 
 
-def _auto_block(T, frames, groups, wave_rows=64, waves=8, target=256):
-    """The default block size, restated: the largest multiple of 16 rows up to one
-    workgroup's rows (waves x wave_rows) and the frame that still gives `target` work
-    items, but at least one wave's rows (or the whole frame when it is shorter)."""
+def _auto_block(T, slots, wave_rows=64, waves=8, target=256):
+    """The default block size, restated: one workgroup's rows (waves x wave_rows) or the
+    whole frame when it is shorter; when that gives fewer than `target` work items (slots
+    per block index x blocks per frame), the most blocks per frame that keep the items at
+    `target` or fewer, of balanced size (ceil(T / n) rounded up to 16 rows), but at least
+    one wave's rows."""
     top = min(T, waves * wave_rows)
-    for bq in range(top, wave_rows - 1, -16):
-        if groups * -(-T // bq) >= target:
-            return bq
-    return min(top, wave_rows)
+    if top <= wave_rows:
+        return top
+    if slots * -(-T // top) >= target:
+        return top
+    n = target // slots
+    bq = 16 * -(-(T // 16) // n)
+    return min(max(bq, wave_rows), top)
 
 
-@pytest.mark.parametrize("name,block_q", [("tiny", 32), ("small", 64), ("720p", 256),
+@pytest.mark.parametrize("name,block_q", [("tiny", 32), ("small", 112), ("720p", 256),
                                           ("1080p", 256), ("stress", 256)])
 def test_plan_query_blocks_cover_the_frame(L, name, block_q):
     wl = W.ALL[name]
     p = Plan.for_workload(wl)
     T = wl.tokens_per_frame
-    assert block_q == _auto_block(T, wl.frames, wl.batch * wl.heads * (wl.frames + 1),
-                                  wave_rows=32)
+    slots = wl.batch * wl.heads * (wl.frames + 1 + p.info["split_frames"])
+    assert block_q == _auto_block(T, slots, wave_rows=32)
     assert p.info["wave_rows"] == 32
     nqb = -(-T // block_q)
     assert p.info["block_q"] == block_q and block_q % 16 == 0
@@ -104,7 +109,9 @@ def test_plan_query_blocks_cover_the_frame(L, name, block_q):
     assert p.info["items"] == wl.batch * wl.heads * (wl.frames + 1 + p.info["split_frames"]) * nqb
     off = Plan.for_workload(wl, key_split=-1)
     assert off.info["split_frames"] == 0
-    assert off.info["items"] == wl.batch * wl.heads * (wl.frames + 1) * nqb
+    off_slots = wl.batch * wl.heads * (wl.frames + 1)
+    assert off.info["block_q"] == _auto_block(T, off_slots, wave_rows=32)
+    assert off.info["items"] == off_slots * -(-T // off.info["block_q"])
 
 
 def test_active_pairs_match_oracle_and_golden(L):
