@@ -96,10 +96,11 @@ int sfa_plan_create(const sfa_geometry* geom, sfa_plan** out);
 /* Tuning overrides for sfa_plan_create_ex; 0 in a field selects the default. */
 typedef struct sfa_plan_options {
   int32_t block_q;        /* query rows per work item: a multiple of 16, at most
-                             waves_per_item * wave_rows, cut to T (default: that maximum,
-                             or less when the launch would otherwise have fewer work items
-                             than 256 compute units); when it does not divide T, the last
-                             item of each frame takes the rows left */
+                             waves_per_item * wave_rows, cut to T (default: that maximum;
+                             when it gives fewer work items than 256 compute units, each
+                             frame is cut into the most blocks of balanced size that keep
+                             the items at 256 or fewer, not below wave_rows); when it does
+                             not divide T, the last item of each frame takes the rows left */
   int32_t waves_per_item; /* 8 (default: two waves per SIMD), 12 (three per SIMD, 32 query
                              rows each, 96-key LDS stages) or 4 (one wave per SIMD, 512
                              registers, 64 query rows per wave) */
