@@ -32,10 +32,11 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (no sparsity)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_720p_traffic.json")
 KERNEL_SOURCES = ("sparse_attention_frame_amd/csrc/sfa_attn.h",
                   "sparse_attention_frame_amd/csrc/sfa_fwd.hip",
+                  "sparse_attention_frame_amd/csrc/sfa_gfx950.h",
                   "sparse_attention_frame_amd/csrc/sfa_internal.h")
 CLOCK_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_720p_clock.json")
 PRO_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prologue_kernel_720p_traffic.json")
-PRO_SOURCES = ("sparse_attention_frame_amd/csrc/sfa_attn.h",
+PRO_SOURCES = ("sparse_attention_frame_amd/csrc/sfa_gfx950.h",
                "sparse_attention_frame_amd/csrc/sfa_prologue.hip",
                "sparse_attention_frame_amd/csrc/sfa_internal.h")
 

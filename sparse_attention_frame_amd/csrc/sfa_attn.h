@@ -49,21 +49,13 @@
 // Granules then go from HBM straight into LDS by DMA (buffer_load_dwordx4 ... lds: no
 // registers, no VALU), 1 KB of contiguous bytes per request, in NBUF rotating 64-key stages;
 // 16 lanes reading one operand hit 16 distinct 16-byte bank groups.
-#include "sfa_internal.h"
+#include "sfa_gfx950.h"
 
 namespace {
 
 using sfa::FwdParams;
 using sfa::Item;
 using sfa::KeyRanges;
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
-typedef __attribute__((address_space(1))) void* global_void_ptr;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // (1.0, 1.0) in bf16: dot2 with it adds the two halves of a packed pair
 constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
@@ -76,13 +68,6 @@ constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 // kLazy makes rescales rare when the scores are wide.
 constexpr float kLazy = 64.0f;
 
-__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  bf16x2 v;
-  v[0] = (__bf16)lo;
-  v[1] = (__bf16)hi;
-  return __builtin_bit_cast(uint32_t, v);
-}
-
 // The larger of a lane's value and that of lane ^ 32 (the other key half of the same
 // query row): one v_permlane32_swap, no LDS round trip.
 __device__ inline float max_xor32(float v) {
@@ -91,12 +76,6 @@ __device__ inline float max_xor32(float v) {
   return fmaxf(__builtin_bit_cast(float, uint32_t(r[0])), __builtin_bit_cast(float, uint32_t(r[1])));
 }
 
-// Wait until at most N of this wave's vector-memory operations (the LDS DMAs
-// of younger stages) are still in flight.
-template <int N>
-__device__ inline void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 template <int D, int WAVES, int QT, int NBUF>
 struct Attn {

@@ -15,7 +15,7 @@
 // 16 features; a head's rotation pairs (e, e + d/2) then sit in the same lane
 // and the same register of two accumulator tiles, and the rotation, the row
 // scale and the bf16 store into q, k or v [b][s][h][e] need no data exchange.
-#include "sfa_attn.h"
+#include "sfa_gfx950.h"
 
 namespace {
 
