@@ -488,6 +488,8 @@ def main():
                      "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic if default_launch else None,
+                     "traffic_gbps": (round(traffic / (fwd_ms * 1e-3) / 1e9, 1)
+                                      if default_launch and traffic else None),
                      "sustained_clock_ghz": (measured_traffic(CLOCK_FILE, key="clock_ghz")
                                              if default_launch else None)},
     }
