@@ -347,8 +347,9 @@ struct Attn {
     }
   }
   // Region with V^T one region ahead: the 8 K reads of QK(j+1) first, then the 16 MFMAs
-  // with 3 VALU ops behind each, and the 8 reads of the next tile's V^T operand placed
-  // after the PV MFMAs that consume the same registers.
+  // with VALU ops behind each (3 on the fixed-maximum path, 4 on the online one), and the
+  // 8 reads of the next tile's V^T operand placed after the PV MFMAs that consume the same
+  // registers.
   template <int VALU>
   __device__ static inline void interleave_kv() {
     __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // DS read: K
@@ -417,9 +418,9 @@ struct Attn {
     const int nst = nfull + (rem > 0 ? 1 : 0);
     if constexpr (NT == 1 && TPS == 2 && (NBUF == 3 || NBUF == 4)) {
       // Tile-level software pipeline over the N = 2*nfull full 32-key tiles:
-      //   region j:  QK(j+1) + PV(j-1)  (16 MFMAs)  ||  softmax(j)  (48 VALU, about 70
-      //   with the online maximum, whose O rescale, if any row moved its maximum, follows
-      //   the region's PV)
+      //   region j:  QK(j+1) + PV(j-1)  (16 MFMAs)  ||  softmax(j)  (48 VALU; some 30
+      //   more with the online maximum, whose O rescale, if any row moved its maximum,
+      //   follows the region's PV)
       // Region j reads K(j+1) for its own QK and V^T(j) for the PV of region j+1,
       // so the V^T reads have a whole region to land. Stage s (tiles 2s, 2s+1)
       // sits in buffer s % NBUF; barrier B_s, just before the region that first
