@@ -292,6 +292,34 @@ def test_largest_frame_count(sfa, limit):
     assert torch.isfinite(out.float()).all()
 
 
+@pytest.mark.parametrize("limit", [40.0, -1.0])
+def test_long_frames(sfa, limit):
+    """Frames of 65536 tokens (4096 granules each; an item of a middle frame streams 12288
+    key granules through its LDS stages, 768 stages of 64 keys), window +-1, a ragged last
+    block in no frame but key halves on the end frames: sampled rows of every frame against
+    the oracle, on the fixed-maximum path and forced online."""
+    F, T, w, H, d = 7, 65536, 1, 1, 128
+    say(f"[long_frames] T={T} limit={limit}")
+    S = (F + 1) * T
+    g = np.random.default_rng(65536)
+    q_np = g.standard_normal((1, S, H, d)).astype(np.float32)
+    k_np = (g.standard_normal((1, S, H, d)) + 3 * g.standard_normal((1, 1, H, d))).astype(
+        np.float32)
+    v_np = g.standard_normal((1, S, H, d)).astype(np.float32)
+    q, k, v = to_dev(q_np, k_np, v_np)
+    q_np, k_np, v_np = (x.float().cpu().numpy() for x in (q, k, v))
+    plan, out, ws = run(sfa, (1, H, d, F, T, w), q, k, v, bound_limit=limit)
+    st, _ = check_stats(sfa, plan, ws, q_np, k_np, bound_limit=limit)
+    assert st["eligible"].all() == (limit > 0)
+    bq = plan.info["block_q"]
+    rows = np.array(sorted({f * T + r for f in range(F + 1)
+                            for r in (0, 31, 32, bq - 1, bq, T // 2 + 5, T - bq, T - 1)}))
+    got = out[0, torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    ref = oracle.attention_rows(q_np, k_np, v_np, F, T, w, 0, 0, rows)
+    assert_close(got[:, 0], ref, f"{len(rows)} rows")
+    assert torch.isfinite(out.float()).all()
+
+
 def test_zero_query_gives_window_mean(sfa):
     F, T, w, H, d = 6, 48, 1, 2, 128
     say("[zero_query]")
